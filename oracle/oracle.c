@@ -1,0 +1,414 @@
+/*
+ * oracle.c -- plain, slow, FP64 CPU oracle for streaming online-softmax attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU-baseline leg of
+ * the benchmark may load this library.  It shares no code, header, table or helper with the
+ * HIP path, and the HIP path never calls it.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [TS]  Tylo.jl docs, "Streaming attention and online state": Online statistics;
+ *         Same-lane conversion; Attention as a consumer.
+ *   [TR]  Tylo.jl docs, "Register fragments and logical axes": Worked softmax;
+ *         Logical types and register packing.
+ *   [WS]  triton-cuda-lab workshop, "A3. Tiled attention with online normalization":
+ *         Keep three quantities for each query row; Trace one query; Masks that preserve
+ *         the recurrence.
+ *   [SK]  Modular MAX Mojo module "fa4_splitk_combine": workspace layout and the per-row-head
+ *         combine formulas.
+ *
+ * Everything is computed in double precision.  Inputs arrive as float32, bfloat16 or float16
+ * element arrays and are widened to double exactly (every such value is a double).
+ *
+ * Tensor layouts: q is [B, Nq, H, D]; k and v are [B, Nkv, H, D], D fastest.  A row-head index
+ * rh = (b * Nq + i) * H + h names one query row of one head.  The optional mask is a row-major
+ * [Nq, Nkv] byte array, nonzero = key visible, shared by every batch and head.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2 };
+enum { OR_NO_NUMERATOR_RESCALE = 1, OR_SAME_BOUNDARY_BF16 = 2, OR_SAME_BOUNDARY_F16 = 4 };
+
+/* ---------------------------------------------------------------------------------------------
+ * Exact widening of stored elements to double.  bfloat16 is the top half of a float32;
+ * float16 is decoded from its IEEE-754 binary16 fields (sign, 5-bit exponent, 10-bit fraction).
+ * ------------------------------------------------------------------------------------------- */
+static double decode_f16_bits(uint16_t h) {
+  int sign = (h >> 15) & 1, e = (h >> 10) & 0x1f, f = h & 0x3ff;
+  double mag;
+  if (e == 0) mag = ldexp((double)f, -24);                 /* subnormal: f * 2^-14 * 2^-10 */
+  else if (e == 31) mag = f ? NAN : INFINITY;
+  else mag = ldexp(1.0 + (double)f / 1024.0, e - 15);
+  return sign ? -mag : mag;
+}
+static double decode_bf16_bits(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float x;
+  memcpy(&x, &u, 4);
+  return (double)x;
+}
+static double load_elem(const void* base, int64_t idx, int dtype) {
+  if (dtype == OR_F32) return (double)((const float*)base)[idx];
+  uint16_t bits = ((const uint16_t*)base)[idx];
+  return dtype == OR_BF16 ? decode_bf16_bits(bits) : decode_f16_bits(bits);
+}
+
+void oracle_decode(const void* src, int dtype, int64_t n, double* dst) {
+  for (int64_t i = 0; i < n; ++i) dst[i] = load_elem(src, i, dtype);
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * O4. Round-to-nearest-even conversion of a float32 to bfloat16 / float16 bits, written from the
+ * definition rather than from bit manipulation: list the two neighbouring representable values
+ * (exact in double), take the nearer, and on a tie the one whose last significand bit is even.
+ * Signed zeros and infinities map to themselves, NaN maps to a NaN, there is no saturation to
+ * the largest finite value and no flush of subnormals ([TS] Same-lane conversion, last
+ * paragraph; [TR] Logical types and register packing).
+ *
+ * A format is (p = significand bits incl. the implicit one, emin = exponent of the smallest
+ * normal, emax = exponent of the largest finite value, ebits).
+ * ------------------------------------------------------------------------------------------- */
+typedef struct { int p, emin, emax, ebits; } fmt_t;
+static const fmt_t FMT_BF16 = {8, -126, 127, 8};
+static const fmt_t FMT_F16 = {11, -14, 15, 5};
+
+static uint16_t encode_small(double mag, int sign, fmt_t f) {
+  /* mag is exactly representable in f (or +inf). */
+  int mbits = f.p - 1, bias = (1 << (f.ebits - 1)) - 1;
+  uint32_t e_field, m_field;
+  if (isinf(mag)) { e_field = (1u << f.ebits) - 1; m_field = 0; }
+  else if (mag == 0.0) { e_field = 0; m_field = 0; }
+  else {
+    int e;
+    frexp(mag, &e);      /* mag = fr * 2^e, fr in [0.5, 1) -> unbiased exponent e-1 */
+    int E = e - 1;
+    if (E < f.emin) {    /* subnormal: mag = m * 2^(emin - mbits) */
+      e_field = 0;
+      m_field = (uint32_t)ldexp(mag, -(f.emin - mbits));
+    } else {
+      e_field = (uint32_t)(E + bias);
+      m_field = (uint32_t)(ldexp(mag, -E) * (double)(1u << mbits)) - (1u << mbits);
+    }
+  }
+  return (uint16_t)((sign << 15) | (e_field << mbits) | m_field);
+}
+
+static uint16_t round_rne(float xf, fmt_t f) {
+  double x = (double)xf;
+  int sign = signbit(x) ? 1 : 0;
+  if (isnan(x)) return (uint16_t)(0x7fff);            /* some quiet NaN (all ones) */
+  double a = fabs(x);
+  if (isinf(a) || a == 0.0) return encode_small(a, sign, f);
+  /* spacing of representable values around a */
+  int e;
+  frexp(a, &e);
+  int E = e - 1;
+  if (E < f.emin) E = f.emin;
+  double ulp = ldexp(1.0, E - (f.p - 1));
+  double lo = floor(a / ulp) * ulp;                   /* exact: a/ulp is exact (power of two) */
+  double hi = lo + ulp;
+  double pick;
+  if (a - lo < hi - a) pick = lo;
+  else if (hi - a < a - lo) pick = hi;
+  else pick = (fmod(lo / ulp, 2.0) == 0.0) ? lo : hi; /* tie: even last significand bit */
+  double maxfin = ldexp(2.0 - ldexp(1.0, -(f.p - 1)), f.emax);
+  if (pick > maxfin) pick = INFINITY;                 /* no saturation */
+  return encode_small(pick, sign, f);
+}
+
+uint16_t oracle_round_bf16(float x) { return round_rne(x, FMT_BF16); }
+uint16_t oracle_round_f16(float x) { return round_rne(x, FMT_F16); }
+
+void oracle_round_array(const float* x, int64_t n, int target_dtype, uint16_t* out) {
+  fmt_t f = target_dtype == OR_BF16 ? FMT_BF16 : FMT_F16;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = round_rne(x[i], f);
+}
+
+/* Same-boundary rounding of a weight: the caller passes the weight already rounded to float32
+ * (the precision in which a kernel holds it); this rounds that float32 to bf16 / f16 and widens
+ * the result back to double. */
+static double round_value(float x, int flags) {
+  uint16_t bits = (flags & OR_SAME_BOUNDARY_BF16) ? oracle_round_bf16(x) : oracle_round_f16(x);
+  return (flags & OR_SAME_BOUNDARY_BF16) ? decode_bf16_bits(bits) : decode_f16_bits(bits);
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Visibility of key j to query i ([WS] Masks that preserve the recurrence: causal includes the
+ * diagonal; [TS] Attention as a consumer: optional Boolean M x N mask; a key index past the
+ * key length is never visible).
+ * ------------------------------------------------------------------------------------------- */
+static int visible(int i, int j, int Nkv, int causal, const uint8_t* mask) {
+  if (j >= Nkv) return 0;
+  if (causal && j > i) return 0;
+  if (mask && mask[(int64_t)i * Nkv + j] == 0) return 0;
+  return 1;
+}
+
+static int64_t qk_index(int b, int t, int h, int N, int H, int D) {
+  return (((int64_t)b * N + t) * H + h) * D;
+}
+
+/* scaled logit s_ij = (q_i . k_j) / sqrt(D)  ([WS] Keep three quantities for each query row) */
+static double logit(const void* q, const void* k, int dt, int b, int i, int j, int h, int Nq, int Nkv,
+                    int H, int D) {
+  int64_t qo = qk_index(b, i, h, Nq, H, D), ko = qk_index(b, j, h, Nkv, H, D);
+  double acc = 0.0;
+  for (int d = 0; d < D; ++d) acc += load_elem(q, qo + d, dt) * load_elem(k, ko + d, dt);
+  return acc / sqrt((double)D);
+}
+
+static void rh_split(int64_t rh, int Nq, int H, int* b, int* i, int* h) {
+  *h = (int)(rh % H);
+  int64_t t = rh / H;
+  *i = (int)(t % Nq);
+  *b = (int)(t / Nq);
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * O1. Dense definition of attention for the selected row-heads.
+ *   vis(i) = visible keys.  If vis(i) is empty: O_i = 0, LSE_i = -inf ([TS] Online statistics:
+ *   entirely masked rows normalize to zero and have log-sum-exp -Inf; [TR] Worked softmax).
+ *   Otherwise M = max_j s_ij, w_j = exp(s_ij - M), L = sum w_j, O_i = sum_j w_j v_j / L and
+ *   LSE_i = M + ln L (natural log).
+ * sel: row-head indices (NULL = all B*Nq*H in order).  out: [nsel, D]; lse: [nsel] (nullable).
+ * ------------------------------------------------------------------------------------------- */
+int oracle_attn_dense(const void* q, const void* k, const void* v, int dt, const uint8_t* mask,
+                      int B, int H, int Nq, int Nkv, int D, int causal, const int64_t* sel,
+                      int64_t nsel, double* out, double* lse) {
+  if (!sel) nsel = (int64_t)B * Nq * H;
+  int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nsel; ++r) {
+    int64_t rh = sel ? sel[r] : r;
+    int b, i, h;
+    rh_split(rh, Nq, H, &b, &i, &h);
+    double* s = (double*)malloc(sizeof(double) * (Nkv > 0 ? Nkv : 1));
+    if (!s) { err = 1; continue; }
+    double* o = out + r * D;
+    int any = 0;
+    double M = -INFINITY;
+    for (int j = 0; j < Nkv; ++j) {
+      if (!visible(i, j, Nkv, causal, mask)) continue;
+      s[j] = logit(q, k, dt, b, i, j, h, Nq, Nkv, H, D);
+      if (!any || s[j] > M) M = s[j];
+      any = 1;
+    }
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    if (!any) {
+      if (lse) lse[r] = -INFINITY;
+      free(s);
+      continue;
+    }
+    double L = 0.0;
+    for (int j = 0; j < Nkv; ++j) {
+      if (!visible(i, j, Nkv, causal, mask)) continue;
+      double w = exp(s[j] - M);
+      L += w;
+      int64_t vo = qk_index(b, j, h, Nkv, H, D);
+      for (int d = 0; d < D; ++d) o[d] += w * load_elem(v, vo + d, dt);
+    }
+    for (int d = 0; d < D; ++d) o[d] /= L;
+    if (lse) lse[r] = M + log(L);
+    free(s);
+  }
+  return err;
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * O2. The chunked online recurrence over BN-key tiles, in the order the workshop's loop states
+ * it ([WS] Keep three quantities for each query row), with the empty state (-inf, 0) and the
+ * guards that keep an all-masked tile from producing -inf - (-inf) ([TS] Online statistics;
+ * [TR] Worked softmax: shift_logit / normalize_weight):
+ *     m' = max(m, max_j s_j);   m_use = (m' == -inf) ? 0 : m'
+ *     alpha = exp(m - m_use);   p_j = exp(s_j - m_use)   (masked s_j = -inf gives p_j = 0)
+ *     l = alpha*l + sum_j p_j;  a = alpha*a + sum_j p_j v_j;  m = m'
+ *   finish: O = (l == 0) ? 0 : a / l;  LSE = (l == 0) ? -inf : m + ln l.
+ * flags: OR_NO_NUMERATOR_RESCALE drops the alpha on a (the bug the trace exposes, which gives 7
+ * instead of 6); OR_SAME_BOUNDARY_* rounds p_j to bf16/f16 before p_j v_j while l keeps the
+ * unrounded p_j ([TS] Attention as a consumer: probability rounding before PV, FP32
+ * denominator).  tile_trace (nullable) receives (m, l, a[0], alpha) after every tile.
+ * ------------------------------------------------------------------------------------------- */
+static void online_core(const double* s, const double* vrows, int n, int D, int BN, int flags,
+                        double* o, double* lse, double* tile_trace) {
+  double m = -INFINITY, l = 0.0;
+  double* a = (double*)calloc((size_t)D, sizeof(double));
+  int tile = 0;
+  for (int j0 = 0; j0 < n; j0 += BN, ++tile) {
+    int j1 = j0 + BN < n ? j0 + BN : n;
+    double mx = -INFINITY;
+    for (int j = j0; j < j1; ++j) if (s[j] > mx) mx = s[j];
+    double m_new = m > mx ? m : mx;
+    double m_use = (m_new == -INFINITY) ? 0.0 : m_new;
+    double alpha = exp(m - m_use);
+    double psum = 0.0;
+    l *= alpha;
+    if (!(flags & OR_NO_NUMERATOR_RESCALE))
+      for (int d = 0; d < D; ++d) a[d] *= alpha;
+    for (int j = j0; j < j1; ++j) {
+      double p = exp(s[j] - m_use);
+      psum += p;
+      double pv = (flags & (OR_SAME_BOUNDARY_BF16 | OR_SAME_BOUNDARY_F16)) ? round_value((float)p, flags) : p;
+      for (int d = 0; d < D; ++d) a[d] += pv * vrows[(int64_t)j * D + d];
+    }
+    l += psum;
+    m = m_new;
+    if (tile_trace) {
+      tile_trace[4 * tile + 0] = m;
+      tile_trace[4 * tile + 1] = l;
+      tile_trace[4 * tile + 2] = a[0];
+      tile_trace[4 * tile + 3] = alpha;
+    }
+  }
+  for (int d = 0; d < D; ++d) o[d] = (l == 0.0) ? 0.0 : a[d] / l;
+  if (lse) *lse = (l == 0.0) ? -INFINITY : m + log(l);
+  free(a);
+}
+
+/* Logits-in entry point for the worked trace: s[n] are already-scaled logits (-inf = masked),
+ * v[n][D] the value rows. */
+void oracle_online_from_logits(const double* s, const double* v, int n, int D, int BN, int flags,
+                               double* out, double* lse, double* tile_trace) {
+  online_core(s, v, n, D, BN, flags, out, lse, tile_trace);
+}
+
+int oracle_attn_online(const void* q, const void* k, const void* v, int dt, const uint8_t* mask,
+                       int B, int H, int Nq, int Nkv, int D, int causal, int BN, int flags,
+                       const int64_t* sel, int64_t nsel, double* out, double* lse) {
+  if (!sel) nsel = (int64_t)B * Nq * H;
+  if (BN < 1) return 1;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nsel; ++r) {
+    int64_t rh = sel ? sel[r] : r;
+    int b, i, h;
+    rh_split(rh, Nq, H, &b, &i, &h);
+    double* s = (double*)malloc(sizeof(double) * (Nkv > 0 ? Nkv : 1));
+    double* vr = (double*)malloc(sizeof(double) * ((int64_t)(Nkv > 0 ? Nkv : 1) * D));
+    for (int j = 0; j < Nkv; ++j) {
+      s[j] = visible(i, j, Nkv, causal, mask) ? logit(q, k, dt, b, i, j, h, Nq, Nkv, H, D) : -INFINITY;
+      int64_t vo = qk_index(b, j, h, Nkv, H, D);
+      for (int d = 0; d < D; ++d) vr[(int64_t)j * D + d] = load_elem(v, vo + d, dt);
+    }
+    online_core(s, vr, Nkv, D, BN, flags, out + r * D, lse ? lse + r : NULL, NULL);
+    free(s);
+    free(vr);
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * O3a. softmax_merge of two independent summaries (m, l, a) ([TS] Online statistics: the merge
+ * of two summaries, returning the rescale factor of each numerator):
+ *   m = max(m1, m2); alpha_k = exp(m_k - m) (0 for an empty summary);
+ *   l = alpha1 l1 + alpha2 l2;  a = alpha1 a1 + alpha2 a2.  Two empty inputs give an empty result.
+ * ------------------------------------------------------------------------------------------- */
+void oracle_merge_nat(double m1, double l1, const double* a1, double m2, double l2, const double* a2,
+                      int D, double* m, double* l, double* a, double* alpha1, double* alpha2) {
+  double mm = m1 > m2 ? m1 : m2;
+  double al1 = (m1 == -INFINITY) ? 0.0 : exp(m1 - mm);
+  double al2 = (m2 == -INFINITY) ? 0.0 : exp(m2 - mm);
+  *m = mm;
+  *l = al1 * l1 + al2 * l2;
+  for (int d = 0; d < D; ++d) a[d] = al1 * a1[d] + al2 * a2[d];
+  *alpha1 = al1;
+  *alpha2 = al2;
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * O3b. The LSE-weighted combine of a split-K workspace, base 2 throughout ([SK] per-row-head
+ * formulas): for each row-head, m* = max_p lse_p; G = log2(sum_p 2^(lse_p - m*)) + m*;
+ * scale_p = 2^(lse_p - G); O[d] = sum_p scale_p * o_partial[p, rh, d].  A partition with
+ * lse_p = -inf gets scale 0; when every partition is empty the output is 0 and G = -inf (the
+ * all-masked convention of [TR] Worked softmax applied to the combine).
+ * o_partial: [P, RH, D]; lse_partial: [P, RH]; out: [RH, D]; g_out (nullable): [RH], base 2.
+ * ------------------------------------------------------------------------------------------- */
+void oracle_combine_log2(const double* o_partial, const double* lse_partial, int P, int64_t RH, int D,
+                         double* out, double* g_out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t rh = 0; rh < RH; ++rh) {
+    double ms = -INFINITY;
+    for (int p = 0; p < P; ++p) if (lse_partial[(int64_t)p * RH + rh] > ms) ms = lse_partial[(int64_t)p * RH + rh];
+    double* o = out + rh * D;
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    if (ms == -INFINITY) {
+      if (g_out) g_out[rh] = -INFINITY;
+      continue;
+    }
+    double sum = 0.0;
+    for (int p = 0; p < P; ++p) {
+      double lp = lse_partial[(int64_t)p * RH + rh];
+      sum += (lp == -INFINITY) ? 0.0 : exp2(lp - ms);
+    }
+    double G = log2(sum) + ms;
+    for (int p = 0; p < P; ++p) {
+      double lp = lse_partial[(int64_t)p * RH + rh];
+      double sc = (lp == -INFINITY) ? 0.0 : exp2(lp - G);
+      const double* op = o_partial + ((int64_t)p * RH + rh) * D;
+      for (int d = 0; d < D; ++d) o[d] += sc * op[d];
+    }
+    if (g_out) g_out[rh] = G;
+  }
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * O3c. The split-K producer's workspace ([SK] workspace layout): key partition p covers
+ * [p*c, min((p+1)*c, Nkv)) with c = ceil(Nkv / P).  For each partition, the dense definition
+ * restricted to the partition's visible keys gives the locally normalised O_p / l_p and
+ * lse_p = log2 of the partition's sum of exponentials = (M + ln L) / ln 2.  An empty partition
+ * gives o_partial = 0 and lse_partial = -inf.
+ * o_partial: [P, nsel, D]; lse_partial: [P, nsel] (base 2).
+ * ------------------------------------------------------------------------------------------- */
+int oracle_splitk(const void* q, const void* k, const void* v, int dt, const uint8_t* mask, int B,
+                  int H, int Nq, int Nkv, int D, int causal, int P, const int64_t* sel, int64_t nsel,
+                  double* o_partial, double* lse_partial) {
+  if (!sel) nsel = (int64_t)B * Nq * H;
+  if (P < 1) return 1;
+  int64_t c = ((int64_t)Nkv + P - 1) / P;
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+  for (int p = 0; p < P; ++p) {
+    for (int64_t r = 0; r < nsel; ++r) {
+      int64_t rh = sel ? sel[r] : r;
+      int b, i, h;
+      rh_split(rh, Nq, H, &b, &i, &h);
+      int64_t j0 = (int64_t)p * c, j1 = j0 + c < Nkv ? j0 + c : Nkv;
+      double* o = o_partial + ((int64_t)p * nsel + r) * D;
+      for (int d = 0; d < D; ++d) o[d] = 0.0;
+      double M = -INFINITY;
+      int any = 0;
+      for (int64_t j = j0; j < j1; ++j) {
+        if (!visible(i, (int)j, Nkv, causal, mask)) continue;
+        double s = logit(q, k, dt, b, i, (int)j, h, Nq, Nkv, H, D);
+        if (!any || s > M) M = s;
+        any = 1;
+      }
+      if (!any) {
+        lse_partial[(int64_t)p * nsel + r] = -INFINITY;
+        continue;
+      }
+      double L = 0.0;
+      for (int64_t j = j0; j < j1; ++j) {
+        if (!visible(i, (int)j, Nkv, causal, mask)) continue;
+        double w = exp(logit(q, k, dt, b, i, (int)j, h, Nq, Nkv, H, D) - M);
+        L += w;
+        int64_t vo = qk_index(b, (int)j, h, Nkv, H, D);
+        for (int d = 0; d < D; ++d) o[d] += w * load_elem(v, vo + d, dt);
+      }
+      for (int d = 0; d < D; ++d) o[d] /= L;
+      lse_partial[(int64_t)p * nsel + r] = (M + log(L)) / log(2.0);
+    }
+  }
+  return 0;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
