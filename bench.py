@@ -1,0 +1,222 @@
+"""Benchmark of the streaming-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one pass over every kernel of the path, on resident synthetic inputs:
+    1. attn_fwd          causal prefill B4 H32 N4096 D128 bf16      (tiled matrix-core kernel)
+    2. attn_fwd_splitk   decode B8 H32 Nq1 Nkv32768 D128 bf16, P=16 (bandwidth kernel)
+    3. attn_combine      merge of that P=16 workspace into the bf16 output
+`value` is the prefill's throughput in TFLOP/s of algorithmic work (4*D per visible
+query-key pair, causal diagonal included); the decode and combine bandwidths are reported
+beside it, together with a decode sweep over P in {4, 8, 16, 37} and a combine measured on a
+workspace too large for the caches.  Every per-kernel time comes from HIP events recorded on the
+stream the kernels are launched on, over the whole timed region.  Rank 0 prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import seeded_inputs as si  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+METRIC = "attn TFLOP/s (% bf16 MFMA peak) B4 H32 N4096 D128 causal; combine GB/s"
+
+
+def prefill_flops(B, H, N, D):
+    pairs = N * (N + 1) // 2                     # causal pairs, diagonal included
+    return 4.0 * D * pairs * B * H
+
+
+def decode_bytes(B, H, Nkv, D, P):
+    kv = 2 * B * Nkv * H * D * 2                 # K and V, bf16
+    q = B * H * D * 2
+    egress = P * B * H * (D + 1) * 4             # o_partial + lse_partial, fp32
+    return kv + q + egress
+
+
+def combine_bytes(P, RH, D, out_elem=2):
+    return P * RH * (D + 1) * 4 + RH * D * out_elem + RH * 4
+
+
+def timed_events(fn_list, steps, warmup):
+    """Run the list of callables once per step; returns (wall seconds for `steps` steps,
+    per-callable mean milliseconds from events on the current stream)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for fn in fn_list:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fn_list]
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for j, fn in enumerate(fn_list):
+            ev[s][j][0].record(stream)
+            fn()
+            ev[s][j][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(steps)])) for j in range(len(fn_list))]
+    return wall, ms
+
+
+def cpu_baseline(q, k, v, budget_s=15.0):
+    """The FP64 oracle (dense definition, OpenMP over rows) on a seeded sample of the prefill
+    workload's query rows, scaled to TFLOP/s of the same algorithmic work."""
+    import oracle
+    s = si.PREFILL
+    B, N, H, D = s["B"], s["N"], s["H"], s["D"]
+    rng = si.rng_for(99, 0)
+    perm = rng.permutation(B * N * H)
+
+    def run(rows):
+        i = (rows // H) % N
+        flops = float(np.sum(4.0 * D * (i + 1)))
+        t0 = time.perf_counter()
+        oracle.attn_dense(q, k, v, causal=True, rows=rows)
+        return flops, time.perf_counter() - t0
+
+    f0, t0 = run(perm[:512])                     # calibration
+    n = int(min(len(perm) - 512, max(512, 512 * (budget_s / max(t0, 1e-3)))))
+    rows = perm[512:512 + n]
+    f, t = run(rows)
+    return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} seeded query rows (of {B * N * H} row-heads) of the causal prefill "
+                      f"B4 H32 N4096 D128 bf16 workload, FP64 dense definition, {t:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "combine"], default=None,
+                    help="time a single kernel (for profiler runs); the JSON line is still printed")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is described, not built)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    import streaming_online_softmax_amd as sa
+
+    dev = torch.device("cuda:0")
+    # ---- inputs (seeded, synthetic, resident in HBM before timing) -----------------------
+    sp = si.PREFILL
+    qc, kc, vc = si.prefill_inputs()
+    q, k, v = qc.to(dev), kc.to(dev), vc.to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    sd = si.DECODE
+    dq, dk, dv = (t.to(dev) for t in si.decode_inputs())
+    P_STEP = 16
+    RH = sd["B"] * sd["H"]
+    o_p = torch.empty((P_STEP, RH, sd["D"]), dtype=torch.float32, device=dev)
+    l_p = torch.empty((P_STEP, RH), dtype=torch.float32, device=dev)
+    dout = torch.empty((RH, sd["D"]), dtype=torch.bfloat16, device=dev)
+    dlse = torch.empty((RH,), dtype=torch.float32, device=dev)
+
+    def k_prefill():
+        sa.attn_fwd(q, k, v, out, lse, causal=True)
+
+    def k_decode():
+        sa.attn_fwd_splitk(dq, dk, dv, P_STEP, o_p.view(P_STEP, sd["B"], sd["H"], sd["D"]),
+                           l_p.view(P_STEP, sd["B"], sd["H"]))
+
+    def k_combine():
+        sa.attn_combine(o_p.view(P_STEP, sd["B"], sd["H"], sd["D"]), l_p.view(P_STEP, sd["B"], sd["H"]),
+                        dout.view(sd["B"], sd["H"], sd["D"]), dlse.view(sd["B"], sd["H"]))
+
+    fns = {"prefill": [k_prefill], "decode": [k_decode], "combine": [k_decode, k_combine]}.get(
+        args.only, [k_prefill, k_decode, k_combine])
+    torch.cuda.synchronize()
+    wall, ms = timed_events(fns, args.steps, args.warmup)
+    assert not torch.isnan(out).any() and not torch.isnan(dout).any(), "NaN in outputs"
+
+    names = {"prefill": ["prefill"], "decode": ["decode"], "combine": ["decode", "combine"]}.get(
+        args.only, ["prefill", "decode", "combine"])
+    t = dict(zip(names, ms))
+    fl = prefill_flops(sp["B"], sp["H"], sp["N"], sp["D"])
+    res = {}
+    if "prefill" in t:
+        res["prefill_tflops"] = fl / (t["prefill"] * 1e-3) / 1e12
+    if "decode" in t:
+        res["decode_gbs"] = decode_bytes(sd["B"], sd["H"], sd["Nkv"], sd["D"], P_STEP) / (t["decode"] * 1e-3) / 1e9
+    if "combine" in t:
+        res["combine_gbs"] = combine_bytes(P_STEP, RH, sd["D"]) / (t["combine"] * 1e-3) / 1e9
+
+    extra = {}
+    if args.only is None:
+        # ---- decode sweep over P (context) -------------------------------------------------
+        sweep = {}
+        for P in sd["P_list"]:
+            op = torch.empty((P, sd["B"], sd["H"], sd["D"]), dtype=torch.float32, device=dev)
+            lp = torch.empty((P, sd["B"], sd["H"]), dtype=torch.float32, device=dev)
+            ob = torch.empty((sd["B"], sd["H"], sd["D"]), dtype=torch.bfloat16, device=dev)
+            _, m = timed_events([lambda: sa.attn_fwd_splitk(dq, dk, dv, P, op, lp),
+                                 lambda: sa.attn_combine(op, lp, ob)], 10, 3)
+            sweep[str(P)] = {"decode_ms": m[0], "decode_GB/s": decode_bytes(sd["B"], sd["H"], sd["Nkv"], sd["D"], P) / (m[0] * 1e-3) / 1e9,
+                             "combine_ms": m[1], "combine_GB/s": combine_bytes(P, RH, sd["D"]) / (m[1] * 1e-3) / 1e9}
+        extra["decode_sweep"] = sweep
+        # ---- combine on a workspace larger than the caches (rows 8192, heads 32, depth 128) -
+        Pc, rows_c = 16, 8192
+        opc = torch.randn((Pc, rows_c, sd["H"], sd["D"]), dtype=torch.float32, device=dev)
+        lpc = torch.randn((Pc, rows_c, sd["H"]), dtype=torch.float32, device=dev)
+        obc = torch.empty((rows_c, sd["H"], sd["D"]), dtype=torch.bfloat16, device=dev)
+        _, m = timed_events([lambda: sa.attn_combine(opc, lpc, obc)], 10, 3)
+        cb = combine_bytes(Pc, rows_c * sd["H"], sd["D"])
+        extra["combine_large"] = {"P": Pc, "rows": rows_c, "heads": sd["H"], "depth": sd["D"], "ms": m[0],
+                                  "GB/s": cb / (m[0] * 1e-3) / 1e9,
+                                  "hbm_frac": cb / (m[0] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        del opc, lpc, obc
+
+    value = res.get("prefill_tflops")
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal prefill B4 H32 N4096 D128 bf16 [B,N,H,D]",
+                   "step": "attn_fwd(prefill) + attn_fwd_splitk(decode B8 H32 Nq1 Nkv32768 D128 bf16, P=16) + attn_combine",
+                   "B": sp["B"], "H": sp["H"], "N": sp["N"], "D": sp["D"], "causal": True},
+        "kernel_ms": t,
+        "roofline": None,
+        "decode": None if "decode" not in t else {
+            "GB/s": res["decode_gbs"], "hbm_frac": res["decode_gbs"] / PEAK_HBM_GBS, "P": P_STEP},
+        "combine": None if "combine" not in t else {
+            "GB/s": res["combine_gbs"], "P": P_STEP,
+            "note": "workspace just written by the decode producer (cache-resident at this size)"},
+    }
+    if value is not None:
+        line["roofline"] = {"bound": "mfma", "achieved": value, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": value / PEAK_BF16_TFLOPS, "traffic": None,
+                            "kernel": "attn_fwd_kernel<bf16, D=128, BN=64>",
+                            "work_per_launch": f"{fl:.4e} FLOP (4*D per causal pair)"}
+    line.update(extra)
+    if args.only is None and not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(qc, kc, vc)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,142 @@
+/*
+ * attn.h -- C ABI of libattn.so: streaming (online-softmax) attention for AMD MI355X (gfx950).
+ *
+ * Three operations, each a hand-written HIP kernel enqueued on the caller's stream:
+ *
+ *   attn_fwd         out = softmax(Q K^T / sqrt(D)) V over visible keys, computed tile by tile
+ *                    with the online-softmax recurrence (running max m, FP32 denominator l, FP32
+ *                    numerator rescaled by alpha = exp(m - m')), never forming the N x N scores.
+ *                    Sources: triton-cuda-lab workshop "A3. Tiled attention with online
+ *                    normalization", sections "Keep three quantities for each query row" and
+ *                    "Masks that preserve the recurrence"; Tylo.jl "Streaming attention and
+ *                    online state", sections "Online statistics" and "Attention as a consumer".
+ *   attn_fwd_splitk  the same recurrence over P contiguous key partitions, writing each
+ *                    partition's locally normalised O_p / l_p and its base-2 log-sum-exp to a
+ *                    workspace.  Source: Modular MAX "fa4_splitk_combine", workspace layout.
+ *   attn_combine     the LSE-weighted merge of such a workspace.  Source: Modular MAX
+ *                    "fa4_splitk_combine", per-row-head formulas (base 2 throughout).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library allocates
+ *     nothing, keeps no state between calls and may be called from several threads at once.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous: ATTN_OK
+ *     means "arguments valid, kernels enqueued".  A fault inside a kernel surfaces at the
+ *     caller's next synchronisation on that stream.
+ *   - On any non-OK return nothing has been enqueued and nothing written;
+ *     attn_last_error() returns a message for the calling thread.  No C++ exception crosses
+ *     this boundary.
+ *   - Layouts are contiguous, D fastest: q and out are [B, Nq, H, D]; k and v are [B, Nkv, H, D].
+ *     A row-head is one query row of one head, rh = (b * Nq + i) * H + h.
+ *   - q, k, v share one element type (ATTN_BF16 or ATTN_FP16); `out` of attn_fwd uses it too,
+ *     rounded to nearest even.  Scores, the softmax state, accumulation and every LSE are FP32.
+ *     The weights p are rounded to the input type (nearest even) before the P.V product while
+ *     the denominator sums the unrounded FP32 p (Tylo "Attention as a consumer").
+ *   - The score scale is fixed at 1/sqrt(D).
+ *   - Visibility of key j to query i: j < Nkv, and (causal == 0 or j <= i), and
+ *     (mask == NULL or mask[i * Nkv + j] != 0).  The mask is a row-major uint8 [Nq, Nkv] array,
+ *     one byte per element, shared by every batch and head.  A row with no visible key gives
+ *     output 0 and LSE -inf (Tylo "Online statistics", all-masked rows).
+ *   - Supported head dimensions D: 16, 32, 64, 128, 256.  B, H, N >= 1.
+ *   - q, k, v, out and o_partial must be 16-byte aligned (128-bit loads and stores).
+ *   - Input values must be finite; NaN or infinite inputs are outside the contract.
+ */
+#ifndef STREAMING_ATTN_H
+#define STREAMING_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+#define ATTN_P_MAX 256 /* largest split count: one partition per MI355X compute unit */
+
+enum attn_dtype { ATTN_BF16 = 0, ATTN_FP16 = 1, ATTN_FP32 = 2 /* combine output only */ };
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_E_NULL = 1,        /* a required pointer is NULL */
+  ATTN_E_SHAPE = 2,       /* a size is < 1, sizes overflow, or causal with Nq != Nkv */
+  ATTN_E_UNSUPPORTED = 3, /* D, dtype, P or block size outside the supported set */
+  ATTN_E_ALIGN = 4,       /* a pointer lacks the required alignment */
+  ATTN_E_WORKSPACE = 5,   /* split-K workspace pointers missing */
+  ATTN_E_HIP = 6          /* the HIP runtime refused a launch; see attn_last_error() */
+};
+
+/*
+ * attn_fwd -- square attention (Nq = Nkv = N).
+ *   q, k, v   [B, N, H, D] of `dtype`, read only.
+ *   out       [B, N, H, D] of `dtype`, written: O_i = sum_j p_ij v_j / l_i, 0 for an all-masked row.
+ *   lse       nullable; [B, N, H] float32, written: NATURAL-log log-sum-exp of the scaled
+ *             logits over the visible keys, -inf for an all-masked row.
+ *   causal    0 or 1 (key j visible to query i only if j <= i; the diagonal is included).
+ *   mask      nullable; uint8 [N, N] as above.
+ *   dtype     ATTN_BF16 or ATTN_FP16.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int N,
+             int D, int causal, const uint8_t* mask, int dtype, void* stream);
+
+/*
+ * attn_fwd_splitk -- the recurrence over P key partitions (Modular MAX "fa4_splitk_combine").
+ *   Partition p covers keys [p*c, min((p+1)*c, Nkv)) with c = ceil(Nkv / P); a partition may be
+ *   empty, or have no key visible to a row.
+ *   q            [B, Nq, H, D]; k, v [B, Nkv, H, D] of `dtype`.
+ *   o_partial    [P, B*Nq, H, D] float32, written: the partition's locally normalised O_p / l_p,
+ *                exactly 0 when the partition has no visible key for that row-head.
+ *   lse_partial  [P, B*Nq, H] float32, written: BASE-2 log-sum-exp m2 + log2(l_p), where m2 is
+ *                the running maximum of the logits in log2 units (logit * log2(e)); -inf when
+ *                the partition has no visible key for that row-head.
+ *   out, lse     nullable.  When out != NULL, attn_combine(o_partial, lse_partial, out, lse, P,
+ *                B*Nq, H, D, dtype, stream) is enqueued right after, in stream order.
+ *   causal       requires Nq == Nkv (rectangular causal has no defined offset: ATTN_E_SHAPE).
+ *   P            1 .. ATTN_P_MAX.
+ *   Nq == 1 runs a bandwidth-bound decode kernel (one workgroup per row-head and partition);
+ *   Nq > 1 runs the tiled matrix-core kernel once per partition.
+ */
+int attn_fwd_splitk(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                    int Nq, int Nkv, int D, int causal, const uint8_t* mask, int P, float* o_partial,
+                    float* lse_partial, int dtype, void* stream);
+
+/*
+ * attn_combine -- merge a split-K workspace (Modular MAX "fa4_splitk_combine"):
+ *   for each row-head rh of rows*heads:  m* = max_p lse_p;  G = log2(sum_p 2^(lse_p - m*)) + m*;
+ *   scale_p = 2^(lse_p - G);  out[rh, d] = sum_p scale_p * o_partial[p, rh, d].
+ *   o_partial    [P, rows, heads, depth] float32 (locally normalised partials), read only.
+ *   lse_partial  [P, rows, heads] float32, base 2, read only.  -inf marks an empty partition,
+ *                which contributes nothing; if every partition is -inf, out = 0 and lse = -inf.
+ *   out          [rows, heads, depth] of out_dtype (ATTN_BF16, ATTN_FP16 or ATTN_FP32).
+ *   lse_out      nullable; [rows, heads] float32, NATURAL log (G * ln 2), comparable with the
+ *                lse of attn_fwd.
+ *   depth        16, 32, 64, 128 or 256.  P in 1 .. ATTN_P_MAX.  P = 4, 8 and 16 run fully
+ *                unrolled instantiations; any other P runs the runtime-P instantiation.
+ */
+int attn_combine(const float* o_partial, const float* lse_partial, void* out, float* lse_out, int P,
+                 int rows, int heads, int depth, int out_dtype, void* stream);
+
+/* Extended forward call for tests and tuning: every attn_fwd argument plus the key-tile width. */
+struct attn_fwd_args {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;          /* nullable */
+  const uint8_t* mask; /* nullable */
+  int B, H, N, D;
+  int causal;
+  int dtype;
+  int block_n;         /* key-tile width: 0 = library default, else 32 or 64 (32 only for D <= 64) */
+};
+int attn_fwd_ex(const struct attn_fwd_args* a, void* stream);
+
+/* Message describing the calling thread's last non-OK return ("" if none). */
+const char* attn_last_error(void);
+
+/* ATTN_ABI_VERSION of the loaded library. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STREAMING_ATTN_H */

@@ -1,0 +1,166 @@
+"""Streaming (online-softmax) attention for AMD MI355X: Python binding of libattn.so.
+
+The binding only marshals arguments: every step of the computation runs in the HIP kernels of
+libattn.so (built from ``csrc/`` by ``build.py``).  torch supplies device memory and streams.
+If the library has not been built, importing the binding raises -- there is no fallback.
+
+Entry points (same names as the C ABI in include/attn.h):
+    attn_fwd(q, k, v, out, lse=None, causal=False, mask=None, block_n=0, stream=None)
+    attn_fwd_splitk(q, k, v, P, o_partial, lse_partial, out=None, lse=None, causal=False,
+                    mask=None, stream=None)
+    attn_combine(o_partial, lse_partial, out, lse_out=None, stream=None)
+    attn_last_error(), attn_abi_version()
+Tensors are torch tensors on the GPU, contiguous, laid out as the header states
+(q/out [B, Nq, H, D]; k/v [B, Nkv, H, D]; o_partial [P, B*Nq, H, D]; lse_partial [P, B*Nq, H]).
+Allocating helpers fwd(), splitk() and combine() return fresh outputs.
+"""
+import ctypes
+import os
+import re
+
+import torch  # noqa: F401  (loads the HIP runtime that libattn.so then binds to)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "attn.h")
+
+ATTN_BF16, ATTN_FP16, ATTN_FP32 = 0, 1, 2
+STATUS = {0: "ATTN_OK", 1: "ATTN_E_NULL", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUPPORTED",
+          4: "ATTN_E_ALIGN", 5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
+P_MAX = 256
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("mask", ctypes.c_void_p),
+                ("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int), ("D", ctypes.c_int),
+                ("causal", ctypes.c_int), ("dtype", ctypes.c_int), ("block_n", ctypes.c_int)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m streaming_online_softmax_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, vp]
+    L.attn_fwd.restype = i32
+    L.attn_fwd_splitk.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp, vp, i32, vp]
+    L.attn_fwd_splitk.restype = i32
+    L.attn_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    L.attn_combine.restype = i32
+    L.attn_fwd_ex.argtypes = [ctypes.POINTER(FwdArgs), vp]
+    L.attn_fwd_ex.restype = i32
+    L.attn_last_error.restype = ctypes.c_char_p
+    L.attn_abi_version.restype = i32
+    return L
+
+
+lib = _load()
+
+
+def declared_symbols():
+    """Function names the public header declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(attn_\w+)\s*\(", text, re.M)))
+
+
+def attn_last_error():
+    return lib.attn_last_error().decode()
+
+
+def attn_abi_version():
+    return int(lib.attn_abi_version())
+
+
+def _check(rc):
+    if rc != 0:
+        raise AttnError(rc, attn_last_error())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float16:
+        return ATTN_FP16
+    if t.dtype == torch.float32:
+        return ATTN_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("tensors must be contiguous GPU tensors")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def attn_fwd(q, k, v, out, lse=None, causal=False, mask=None, block_n=0, stream=None):
+    B, N, H, D = q.shape
+    a = FwdArgs(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(mask),
+                B, H, N, D, int(causal), _dtype_code(q), int(block_n))
+    _check(lib.attn_fwd_ex(ctypes.byref(a), _stream(stream)))
+
+
+def attn_fwd_splitk(q, k, v, P, o_partial, lse_partial, out=None, lse=None, causal=False, mask=None,
+                    stream=None):
+    B, Nq, H, D = q.shape
+    Nkv = k.shape[1]
+    _check(lib.attn_fwd_splitk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nkv, D,
+                               int(causal), _ptr(mask), int(P), _ptr(o_partial), _ptr(lse_partial),
+                               _dtype_code(q), _stream(stream)))
+
+
+def attn_combine(o_partial, lse_partial, out, lse_out=None, stream=None):
+    P = o_partial.shape[0]
+    depth = o_partial.shape[-1]
+    heads = o_partial.shape[-2]
+    rows = o_partial[0].numel() // (heads * depth)
+    _check(lib.attn_combine(_ptr(o_partial), _ptr(lse_partial), _ptr(out), _ptr(lse_out), int(P),
+                            rows, heads, depth, _dtype_code(out), _stream(stream)))
+
+
+# ---- allocating helpers -------------------------------------------------------------------
+def fwd(q, k, v, causal=False, mask=None, block_n=0, with_lse=True):
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if with_lse else None
+    attn_fwd(q, k, v, out, lse, causal=causal, mask=mask, block_n=block_n)
+    return out, lse
+
+
+def workspace(q, P):
+    B, Nq, H, D = q.shape
+    o_p = torch.empty((P, B * Nq, H, D), dtype=torch.float32, device=q.device)
+    l_p = torch.empty((P, B * Nq, H), dtype=torch.float32, device=q.device)
+    return o_p, l_p
+
+
+def splitk(q, k, v, P, causal=False, mask=None, combine=True):
+    o_p, l_p = workspace(q, P)
+    out = lse = None
+    if combine:
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn_fwd_splitk(q, k, v, P, o_p, l_p, out=out, lse=lse, causal=causal, mask=mask)
+    return o_p, l_p, out, lse
+
+
+def combine(o_partial, lse_partial, out_dtype=torch.float32):
+    P, RH = lse_partial.shape[0], lse_partial[0].numel()
+    heads = o_partial.shape[-2]
+    out = torch.empty(o_partial.shape[1:], dtype=out_dtype, device=o_partial.device)
+    lse = torch.empty(o_partial.shape[1:-1], dtype=torch.float32, device=o_partial.device)
+    attn_combine(o_partial, lse_partial, out, lse)
+    return out, lse

@@ -1,0 +1,182 @@
+// api.cpp -- the C ABI of libattn.so: argument validation, kernel selection, launch on the
+// caller's stream.  Validation happens before any HIP call, so a rejected call enqueues
+// nothing, writes nothing and touches no device (the pages' rule that unsupported layouts are
+// rejected rather than silently computed differently: Tylo.jl "Streaming attention and online
+// state", section "Same-lane conversion"; workshop "Masks that preserve the recurrence",
+// rectangular causal rejected).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/attn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return ATTN_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool supported_d(int D) { return D == 16 || D == 32 || D == 64 || D == 128 || D == 256; }
+
+float scale_log2(int D) { return (float)(1.4426950408889634 / std::sqrt((double)D)); }
+
+// Shared checks of q/k/v/out sizes.  Returns ATTN_OK or an error code (message set).
+int check_qkv(const void* q, const void* k, const void* v, int B, int H, int Nq, int Nkv, int D,
+              int causal, int dtype) {
+  if (!q || !k || !v) return fail(ATTN_E_NULL, "q, k and v must be non-NULL device pointers");
+  if (B < 1 || H < 1 || Nq < 1 || Nkv < 1) return fail(ATTN_E_SHAPE, "B, H, Nq, Nkv must be >= 1 (got %d, %d, %d, %d)", B, H, Nq, Nkv);
+  if (!supported_d(D)) return fail(ATTN_E_UNSUPPORTED, "head dimension D=%d not supported (16, 32, 64, 128, 256)", D);
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return fail(ATTN_E_UNSUPPORTED, "dtype %d not supported for q/k/v (ATTN_BF16 or ATTN_FP16)", dtype);
+  if (causal != 0 && causal != 1) return fail(ATTN_E_SHAPE, "causal must be 0 or 1 (got %d)", causal);
+  if (causal && Nq != Nkv) return fail(ATTN_E_SHAPE, "causal attention requires Nq == Nkv (got %d, %d): a rectangular causal offset is not defined", Nq, Nkv);
+  const double elems_q = (double)B * Nq * H * D, elems_kv = (double)B * Nkv * H * D;
+  if (elems_q > 9.0e15 || elems_kv > 9.0e15) return fail(ATTN_E_SHAPE, "tensor sizes overflow");
+  if ((double)Nq * Nkv > 9.0e18) return fail(ATTN_E_SHAPE, "mask size overflows");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return fail(ATTN_E_ALIGN, "q, k and v must be 16-byte aligned");
+  return ATTN_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(ATTN_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int do_combine(const float* o_partial, const float* lse_partial, void* out, float* lse_out, int P,
+               int rows, int heads, int depth, int out_dtype, hipStream_t s) {
+  attn::CombineParams cp;
+  cp.o_partial = o_partial;
+  cp.lse_partial = lse_partial;
+  cp.out = out;
+  cp.lse_out = lse_out;
+  cp.P = P;
+  cp.RH = rows * heads;
+  return hip_status(attn::launch_combine(cp, depth, out_dtype, s), "attn_combine launch");
+}
+
+int check_combine(const float* o_partial, const float* lse_partial, void* out, float* lse_out, int P,
+                  int rows, int heads, int depth, int out_dtype) {
+  if (!o_partial || !lse_partial || !out) return fail(ATTN_E_NULL, "o_partial, lse_partial and out must be non-NULL");
+  if (P < 1) return fail(ATTN_E_SHAPE, "P must be >= 1 (got %d)", P);
+  if (P > ATTN_P_MAX) return fail(ATTN_E_UNSUPPORTED, "P=%d exceeds ATTN_P_MAX=%d", P, ATTN_P_MAX);
+  if (rows < 1 || heads < 1) return fail(ATTN_E_SHAPE, "rows and heads must be >= 1");
+  if ((int64_t)rows * heads > 0x7fffffffLL) return fail(ATTN_E_SHAPE, "rows*heads exceeds 2^31-1");
+  if (!supported_d(depth)) return fail(ATTN_E_UNSUPPORTED, "depth=%d not supported (16, 32, 64, 128, 256)", depth);
+  if (out_dtype != ATTN_BF16 && out_dtype != ATTN_FP16 && out_dtype != ATTN_FP32) return fail(ATTN_E_UNSUPPORTED, "out_dtype %d not supported", out_dtype);
+  if (!aligned(o_partial, 16)) return fail(ATTN_E_ALIGN, "o_partial must be 16-byte aligned");
+  if (!aligned(lse_partial, 4) || (lse_out && !aligned(lse_out, 4))) return fail(ATTN_E_ALIGN, "LSE arrays must be 4-byte aligned");
+  if (!aligned(out, 16)) return fail(ATTN_E_ALIGN, "out must be 16-byte aligned");
+  return ATTN_OK;
+}
+
+int fwd_impl(const attn_fwd_args* a, hipStream_t s) {
+  int rc = check_qkv(a->q, a->k, a->v, a->B, a->H, a->N, a->N, a->D, a->causal, a->dtype);
+  if (rc) return rc;
+  if (!a->out) return fail(ATTN_E_NULL, "out must be a non-NULL device pointer");
+  if (!aligned(a->out, 16)) return fail(ATTN_E_ALIGN, "out must be 16-byte aligned");
+  if (a->lse && !aligned(a->lse, 4)) return fail(ATTN_E_ALIGN, "lse must be 4-byte aligned");
+  int BN = a->block_n;
+  if (BN == 0) BN = 64;
+  if (BN != 32 && BN != 64) return fail(ATTN_E_UNSUPPORTED, "block_n=%d not supported (32 or 64)", a->block_n);
+  if (BN == 32 && a->D > 64) return fail(ATTN_E_UNSUPPORTED, "block_n=32 is built for D <= 64 only");
+  const int64_t nqb = ((int64_t)a->N + attn::fwd_block_m() - 1) / attn::fwd_block_m();
+  if (nqb * a->H * a->B > 0x7fffffffLL) return fail(ATTN_E_SHAPE, "grid too large");
+
+  attn::FwdParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v;
+  p.out = a->out; p.lse = a->lse;
+  p.mask = a->mask;
+  p.B = a->B; p.H = a->H; p.Nq = a->N; p.Nkv = a->N;
+  p.causal = a->causal;
+  p.P = 1; p.chunk = a->N;
+  p.n_qblocks = (int)nqb;
+  p.mask_vec = a->mask && aligned(a->mask, 8) && (a->N % 8 == 0);
+  p.scale_log2 = scale_log2(a->D);
+  return hip_status(attn::launch_fwd(p, a->dtype, a->D, BN, false, s), "attn_fwd launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_last_error(void) { return g_err; }
+
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int N,
+             int D, int causal, const uint8_t* mask, int dtype, void* stream) {
+  attn_fwd_args a{};
+  a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.mask = mask;
+  a.B = B; a.H = H; a.N = N; a.D = D; a.causal = causal; a.dtype = dtype; a.block_n = 0;
+  return fwd_impl(&a, (hipStream_t)stream);
+}
+
+int attn_fwd_ex(const struct attn_fwd_args* a, void* stream) {
+  if (!a) return fail(ATTN_E_NULL, "args must be non-NULL");
+  return fwd_impl(a, (hipStream_t)stream);
+}
+
+int attn_fwd_splitk(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                    int Nq, int Nkv, int D, int causal, const uint8_t* mask, int P, float* o_partial,
+                    float* lse_partial, int dtype, void* stream) {
+  int rc = check_qkv(q, k, v, B, H, Nq, Nkv, D, causal, dtype);
+  if (rc) return rc;
+  if (P < 1) return fail(ATTN_E_SHAPE, "P must be >= 1 (got %d)", P);
+  if (P > ATTN_P_MAX) return fail(ATTN_E_UNSUPPORTED, "P=%d exceeds ATTN_P_MAX=%d", P, ATTN_P_MAX);
+  if (!o_partial || !lse_partial) return fail(ATTN_E_WORKSPACE, "o_partial and lse_partial are required");
+  if (!aligned(o_partial, 16)) return fail(ATTN_E_ALIGN, "o_partial must be 16-byte aligned");
+  if (!aligned(lse_partial, 4)) return fail(ATTN_E_ALIGN, "lse_partial must be 4-byte aligned");
+  const int64_t RH = (int64_t)B * Nq * H;
+  if (RH > 0x7fffffffLL) return fail(ATTN_E_SHAPE, "B*Nq*H exceeds 2^31-1");
+  if (out) {
+    rc = check_combine(o_partial, lse_partial, out, lse, P, B * Nq, H, D, dtype);
+    if (rc) return rc;
+  }
+  const int chunk = (int)(((int64_t)Nkv + P - 1) / P);
+  const float c = scale_log2(D);
+  hipStream_t s = (hipStream_t)stream;
+  if (Nq == 1) {
+    if (RH * P > 0x7fffffffLL) return fail(ATTN_E_SHAPE, "grid too large");
+    attn::DecodeParams p{};
+    p.q = q; p.k = k; p.v = v; p.o_partial = o_partial; p.lse_partial = lse_partial; p.mask = mask;
+    p.B = B; p.H = H; p.Nq = Nq; p.Nkv = Nkv; p.causal = causal; p.P = P; p.chunk = chunk; p.scale_log2 = c;
+    rc = hip_status(attn::launch_decode(p, dtype, D, s), "attn_fwd_splitk decode launch");
+  } else {
+    const int64_t nqb = ((int64_t)Nq + attn::fwd_block_m() - 1) / attn::fwd_block_m();
+    if (nqb * H * B * P > 0x7fffffffLL) return fail(ATTN_E_SHAPE, "grid too large");
+    attn::FwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.o_partial = o_partial; p.lse_partial = lse_partial; p.mask = mask;
+    p.B = B; p.H = H; p.Nq = Nq; p.Nkv = Nkv; p.causal = causal; p.P = P; p.chunk = chunk;
+    p.n_qblocks = (int)nqb;
+    p.mask_vec = mask && aligned(mask, 8) && (Nkv % 8 == 0) && (chunk % 8 == 0);
+    p.scale_log2 = c;
+    rc = hip_status(attn::launch_fwd(p, dtype, D, 64, true, s), "attn_fwd_splitk launch");
+  }
+  if (rc || !out) return rc;
+  return do_combine(o_partial, lse_partial, out, lse, P, B * Nq, H, D, dtype, s);
+}
+
+int attn_combine(const float* o_partial, const float* lse_partial, void* out, float* lse_out, int P,
+                 int rows, int heads, int depth, int out_dtype, void* stream) {
+  int rc = check_combine(o_partial, lse_partial, out, lse_out, P, rows, heads, depth, out_dtype);
+  if (rc) return rc;
+  return do_combine(o_partial, lse_partial, out, lse_out, P, rows, heads, depth, out_dtype, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// launch.h -- kernel parameter blocks and launchers (internal to libattn.so).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+constexpr int ATTN_P_MAX_DEV = 256;   // largest split count (one partition per compute unit)
+
+// Tiled matrix-core forward (attn_fwd, and the split-K producer when Nq > 1).
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;            // [B, Nq, H, D] input dtype (unsplit)
+  float* lse;           // [B, Nq, H] natural log, nullable (unsplit)
+  float* o_partial;     // [P, B*Nq, H, D] (split)
+  float* lse_partial;   // [P, B*Nq, H] base 2 (split)
+  const uint8_t* mask;  // [Nq, Nkv] or null
+  int B, H, Nq, Nkv;
+  int causal;
+  int P;                // 1 when unsplit
+  int chunk;            // keys per partition (split)
+  int n_qblocks;        // ceil(Nq / 128)
+  int mask_vec;         // mask rows may be read 8 bytes at a time
+  float scale_log2;     // log2(e) / sqrt(D)
+};
+
+// Bandwidth-bound split-K decode producer (one workgroup per row-head and partition).
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o_partial;
+  float* lse_partial;
+  const uint8_t* mask;
+  int B, H, Nq, Nkv;
+  int causal;
+  int P;
+  int chunk;
+  float scale_log2;
+};
+
+// LSE-weighted combine of a split-K workspace.
+struct CombineParams {
+  const float* o_partial;
+  const float* lse_partial;
+  void* out;
+  float* lse_out;       // natural log, nullable
+  int P;
+  int RH;               // rows * heads
+};
+
+hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int BN, bool split, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int dtype, int D, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, int depth, int out_dtype, hipStream_t s);
+int fwd_block_m();
+
+}  // namespace attn

@@ -1,0 +1,92 @@
+"""The C ABI library loads, exports every declared symbol and rejects bad arguments before any
+HIP call.  CPU only: the reject-path calls use fake, never-dereferenced pointer values, so they
+run only where no GPU is visible (the GPU suite repeats them with real buffers)."""
+import ctypes
+
+import pytest
+import torch
+
+import streaming_online_softmax_amd as sa
+
+E_NULL, E_SHAPE, E_UNSUP, E_ALIGN, E_WS = 1, 2, 3, 4, 5
+
+
+def test_library_exports_every_declared_symbol():
+    names = sa.declared_symbols()
+    assert {"attn_fwd", "attn_fwd_splitk", "attn_combine", "attn_fwd_ex", "attn_last_error",
+            "attn_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(sa.lib, n), n
+
+
+def test_abi_version():
+    assert sa.attn_abi_version() == 1
+
+
+needs_no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                                  reason="fake-pointer reject paths run only where no GPU is visible")
+
+A = 0x10000      # 16-byte aligned fake address (never dereferenced: every call below is rejected)
+BAD = 0x10008    # 8-byte aligned only
+
+
+def fwd(q=A, k=A, v=A, out=A, lse=None, B=1, H=1, N=64, D=64, causal=0, mask=None, dtype=0):
+    return sa.lib.attn_fwd(q, k, v, out, lse, B, H, N, D, causal, mask, dtype, None)
+
+
+def splitk(q=A, k=A, v=A, out=None, lse=None, B=1, H=1, Nq=1, Nkv=64, D=64, causal=0, mask=None, P=4,
+           o_p=A, l_p=A, dtype=0):
+    return sa.lib.attn_fwd_splitk(q, k, v, out, lse, B, H, Nq, Nkv, D, causal, mask, P, o_p, l_p, dtype, None)
+
+
+def combine(o_p=A, l_p=A, out=A, lse=None, P=4, rows=1, heads=1, depth=64, out_dtype=2):
+    return sa.lib.attn_combine(o_p, l_p, out, lse, P, rows, heads, depth, out_dtype, None)
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("call,code", [
+    (lambda: fwd(q=None), E_NULL),
+    (lambda: fwd(out=None), E_NULL),
+    (lambda: fwd(B=0), E_SHAPE),
+    (lambda: fwd(N=0), E_SHAPE),
+    (lambda: fwd(H=-1), E_SHAPE),
+    (lambda: fwd(D=48), E_UNSUP),
+    (lambda: fwd(D=512), E_UNSUP),
+    (lambda: fwd(dtype=2), E_UNSUP),
+    (lambda: fwd(causal=2), E_SHAPE),
+    (lambda: fwd(q=BAD), E_ALIGN),
+    (lambda: fwd(out=BAD), E_ALIGN),
+    (lambda: splitk(causal=1), E_SHAPE),            # rectangular causal is rejected
+    (lambda: splitk(P=0), E_SHAPE),
+    (lambda: splitk(P=257), E_UNSUP),
+    (lambda: splitk(o_p=None), E_WS),
+    (lambda: splitk(l_p=None), E_WS),
+    (lambda: splitk(o_p=BAD), E_ALIGN),
+    (lambda: splitk(D=8), E_UNSUP),
+    (lambda: combine(P=0), E_SHAPE),
+    (lambda: combine(P=300), E_UNSUP),
+    (lambda: combine(depth=100), E_UNSUP),
+    (lambda: combine(out_dtype=7), E_UNSUP),
+    (lambda: combine(out=None), E_NULL),
+    (lambda: combine(o_p=BAD), E_ALIGN),
+    (lambda: combine(rows=0), E_SHAPE),
+])
+def test_reject_paths(call, code):
+    rc = call()
+    assert rc == code, (rc, sa.attn_last_error())
+    assert sa.attn_last_error() != ""
+
+
+@needs_no_gpu
+def test_fwd_ex_rejects_bad_block_n():
+    a = sa.FwdArgs(A, A, A, A, None, None, 1, 1, 64, 128, 0, 0, 32)
+    assert sa.lib.attn_fwd_ex(ctypes.byref(a), None) == E_UNSUP
+    a.block_n = 48
+    assert sa.lib.attn_fwd_ex(ctypes.byref(a), None) == E_UNSUP
+    assert sa.lib.attn_fwd_ex(None, None) == E_NULL
+
+
+def test_binding_refuses_host_tensors():
+    q = torch.zeros(1, 4, 1, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sa.attn_fwd(q, q, q, q)

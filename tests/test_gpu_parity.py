@@ -1,0 +1,306 @@
+"""Parity of the HIP path (through the C ABI) with the FP64 oracle on every workload.
+
+Tolerances: max |O_gpu - O_oracle| <= 2e-2 (bf16) / 5e-3 (fp16) over all compared elements;
+|LSE_gpu - LSE_oracle| <= 1e-3 * max(1, |LSE|); an all-masked row must give O exactly 0 and
+LSE exactly -inf; split-K combined must match the unsplit result to 1e-3.  The oracle is fed the
+exact bf16/fp16 values the kernels read.  Full-size workloads compare sampled rows (seeded),
+which the oracle computes one by one, plus properties that hold at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f16": 5e-3}
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def sa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import streaming_online_softmax_amd as mod
+    return mod
+
+
+def _compare(out, lse, ref, ref_lse, dtype, what=""):
+    """out: [rows, D] GPU result (any float dtype), lse: [rows] natural log."""
+    o = out.float().cpu().numpy().reshape(ref.shape).astype(np.float64)
+    assert not np.isnan(o).any(), f"{what}: NaN in output"
+    err = np.abs(o - ref).max() if o.size else 0.0
+    assert err <= TOL[dtype], f"{what}: max|dO|={err:.3e} > {TOL[dtype]}"
+    empty = ref_lse == -np.inf
+    assert np.all(o[empty] == 0.0), f"{what}: all-masked rows not exactly 0"
+    if lse is not None:
+        l = lse.float().cpu().numpy().reshape(ref_lse.shape).astype(np.float64)
+        assert np.all(l[empty] == -np.inf), f"{what}: all-masked rows LSE not -inf"
+        fin = ~empty
+        lerr = np.abs(l[fin] - ref_lse[fin]) / np.maximum(1.0, np.abs(ref_lse[fin]))
+        assert (lerr.max() if lerr.size else 0.0) <= 1e-3, f"{what}: LSE rel err {lerr.max():.3e}"
+    return err
+
+
+# ---------------------------------------------------------------------------------------------
+# single-head N64 D16 (fp32 draws, run on the bf16 and fp16 casts), BN = 32
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_small_fp32_drawn(sa, dtype):
+    q32, k32, v32 = si.small_inputs()
+    q, k, v = si.cast(q32, dtype), si.cast(k32, dtype), si.cast(v32, dtype)
+    out, lse = sa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), block_n=32)
+    ref, ref_lse = oracle.attn_dense(q, k, v)
+    _compare(out, lse, ref, ref_lse, dtype, f"small {dtype}")
+
+
+# ---------------------------------------------------------------------------------------------
+# single-head sweep: N x D x dtype x causal x BN x variant (360 cases)
+# ---------------------------------------------------------------------------------------------
+_ORACLE_CACHE = {}
+
+
+def _sweep_ref(case, q, k, v):
+    key = (case["N"], case["D"], case["dtype"], case["causal"], case["variant"])
+    if key not in _ORACLE_CACHE:
+        _ORACLE_CACHE.clear()
+        _ORACLE_CACHE[key] = oracle.attn_dense(q, k, v, causal=case["causal"])
+    return _ORACLE_CACHE[key]
+
+
+CASES = si.sweep_cases()
+
+
+def _case_id(c):
+    return f"N{c['N']}-D{c['D']}-{c['dtype']}-{'causal' if c['causal'] else 'full'}-BN{c['BN']}-{c['variant']}"
+
+
+@pytest.mark.parametrize("case", sorted(CASES, key=lambda c: (c["N"], c["D"], c["dtype"], c["causal"], c["variant"], c["BN"])),
+                         ids=_case_id)
+def test_sweep(sa, case):
+    q, k, v = si.sweep_inputs(case)
+    out, lse = sa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=case["causal"], block_n=case["BN"])
+    ref, ref_lse = _sweep_ref(case, q, k, v)
+    _compare(out, lse, ref, ref_lse, case["dtype"], _case_id(case))
+    if case["variant"] == "uniform":
+        # p = 1 for every visible key: l is an exact integer, LSE = ln |vis|
+        N = case["N"]
+        cnt = np.arange(1, N + 1) if case["causal"] else np.full(N, N)
+        np.testing.assert_allclose(lse.cpu().numpy().reshape(-1), np.log(cnt), rtol=1e-6)
+
+
+def test_single_key_is_exact(sa):
+    """N = 1: the only weight is 1, so O equals v0 bit for bit (bf16 in, bf16 out)."""
+    for D in (16, 32, 64, 128, 256):
+        rng = si.rng_for(80, D)
+        q, k, v = (si.cast(x, "bf16") for x in si.draw_qkv(rng, (2, 1, 3, D), (2, 1, 3, D)))
+        out, lse = sa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True)
+        assert torch.equal(out.cpu(), v)
+
+
+# ---------------------------------------------------------------------------------------------
+# causal future-V perturbation (workshop checker)
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("D", [64, 128])
+def test_future_perturbation_bitwise(sa, D):
+    N, i0 = 1000, 437
+    rng = si.rng_for(81, D)
+    q, k, v = (si.cast(x, "bf16") for x in si.draw_qkv(rng, (1, N, 2, D), (1, N, 2, D)))
+    out1, lse1 = sa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True)
+    _, k_new, v_new = si.draw_qkv(si.rng_for(82, D), (1, 1, 1, 1), (1, N - i0 - 1, 2, D))
+    k2, v2 = k.clone(), v.clone()
+    k2[:, i0 + 1:] = si.cast(k_new, "bf16")
+    v2[:, i0 + 1:] = si.cast(v_new, "bf16")
+    out2, lse2 = sa.fwd(q.to(DEV), k2.to(DEV), v2.to(DEV), causal=True)
+    assert torch.equal(out1[:, : i0 + 1], out2[:, : i0 + 1])
+    assert torch.equal(lse1[:, : i0 + 1], lse2[:, : i0 + 1])
+    changed = (out1[:, i0 + 1:] != out2[:, i0 + 1:]).flatten(2).any(dim=2)
+    assert bool(changed.all())
+
+
+# ---------------------------------------------------------------------------------------------
+# multi-head causal prefill B4 H32 N4096 D128 bf16 (the benchmark's launch configuration)
+# ---------------------------------------------------------------------------------------------
+def _sample_rows(rng, B, N, H, n, extra_rows=()):
+    b = rng.integers(0, B, n)
+    i = rng.integers(0, N, n)
+    h = rng.integers(0, H, n)
+    for r in extra_rows:
+        b = np.append(b, [0, B - 1])
+        i = np.append(i, [r, r])
+        h = np.append(h, [0, H - 1])
+    return np.unique((b * N + i) * H + h)
+
+
+def test_prefill_full_size(sa):
+    s = si.PREFILL
+    q, k, v = si.prefill_inputs()
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out, lse = sa.fwd(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any() and bool(torch.isfinite(lse).all())
+    rows = _sample_rows(si.rng_for(83, 0), s["B"], s["N"], s["H"], 384,
+                        extra_rows=(0, 1, 127, 128, 2047, 4095))
+    ref, ref_lse = oracle.attn_dense(q, k, v, causal=True, rows=rows)
+    o = out.reshape(-1, s["D"])[torch.from_numpy(rows).to(DEV)]
+    l = lse.reshape(-1)[torch.from_numpy(rows).to(DEV)]
+    _compare(o, l, ref, ref_lse, "bf16", "prefill")
+
+
+# ---------------------------------------------------------------------------------------------
+# split-K decode B8 H32 Nq1 Nkv32768 D128 bf16, P in {4, 8, 16, 37}
+# ---------------------------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def decode_data(sa):
+    q, k, v = si.decode_inputs()
+    return q, k, v, q.to(DEV), k.to(DEV), v.to(DEV)
+
+
+@pytest.mark.parametrize("P", [4, 8, 16, 37])
+def test_decode_splitk_full_size(sa, decode_data, P):
+    s = si.DECODE
+    q, k, v, qd, kd, vd = decode_data
+    o_p, l_p, out, lse = sa.splitk(qd, kd, vd, P)
+    # unsplit reference on the GPU: one partition (the combine is then the identity)
+    o1, l1, _, _ = sa.splitk(qd, kd, vd, 1, combine=False)
+    out_f32, lse_f32 = sa.combine(o_p, l_p, torch.float32)
+    torch.cuda.synchronize()
+    RH = s["B"] * s["H"]
+    d = (out_f32.reshape(RH, -1) - o1.reshape(RH, -1)).abs().max().item()
+    assert d <= 1e-3, f"split vs unsplit {d:.3e}"
+    rows = np.unique(si.rng_for(84, P).integers(0, RH, 48))
+    ref_op, ref_lp = oracle.splitk(q, k, v, P, rows=rows)
+    rt = torch.from_numpy(rows).to(DEV)
+    for p in range(P):
+        _compare(o_p[p].reshape(RH, -1)[rt], None, ref_op[p], ref_lp[p], "bf16", f"o_partial p={p}")
+        lp = l_p[p].reshape(-1)[rt].cpu().numpy().astype(np.float64)
+        np.testing.assert_allclose(lp, ref_lp[p], rtol=1e-4, atol=1e-4)
+    ref, ref_lse = oracle.attn_dense(q, k, v, rows=rows)
+    _compare(out.reshape(RH, -1)[rt], lse.reshape(-1)[rt], ref, ref_lse, "bf16", f"combined P={P}")
+
+
+def test_decode_empty_partitions(sa):
+    """More partitions than keys: empty partitions give o_partial exactly 0 and lse -inf, and the
+    combine ignores them."""
+    rng = si.rng_for(85, 0)
+    q, k, v = (si.cast(x, "bf16") for x in si.draw_qkv(rng, (2, 1, 3, 128), (2, 17, 3, 128)))
+    o_p, l_p, out, lse = sa.splitk(q.to(DEV), k.to(DEV), v.to(DEV), 37)
+    torch.cuda.synchronize()
+    ref_op, ref_lp = oracle.splitk(q, k, v, 37)
+    empty = ref_lp == -np.inf
+    assert empty.sum() > 0
+    assert np.all(l_p.cpu().numpy().reshape(37, -1)[empty] == -np.inf)
+    assert np.all(o_p.cpu().numpy().reshape(37, 6, -1)[empty] == 0.0)
+    ref, ref_lse = oracle.attn_dense(q, k, v)
+    _compare(out.reshape(6, -1), lse.reshape(-1), ref, ref_lse, "bf16", "decode P>Nkv")
+
+
+@pytest.mark.parametrize("P", [1, 3, 7])
+def test_square_causal_split_matches_unsplit(sa, P):
+    rng = si.rng_for(86, P)
+    N, D = 1000, 64
+    q, k, v = (si.cast(x, "bf16") for x in si.draw_qkv(rng, (2, N, 4, D), (2, N, 4, D)))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o_p, l_p, _, _ = sa.splitk(qd, kd, vd, P, causal=True, combine=False)
+    out32, lse32 = sa.combine(o_p, l_p, torch.float32)
+    out, lse = sa.fwd(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    out32, lse32 = out32.reshape(out.shape), lse32.reshape(lse.shape)   # [B*Nq, H, ...] -> [B, Nq, H, ...]
+    d = (out32 - out.float()).abs()
+    bound = 1e-3 + out32.abs() * 2.0 ** -8          # bf16 output rounding of the unsplit result
+    assert bool((d <= bound).all()), f"split vs unsplit {d.max().item():.3e}"
+    assert torch.allclose(lse32, lse, rtol=1e-5, atol=1e-4)
+    ref, ref_lse = oracle.attn_dense(q, k, v, causal=True)
+    _compare(out32.reshape(-1, D), lse32.reshape(-1), ref, ref_lse, "bf16", f"split P={P}")
+
+
+# ---------------------------------------------------------------------------------------------
+# masked long context B1 H16 N16384 D256: causal AND Bernoulli(0.5) mask, 1/64 rows all-masked
+# ---------------------------------------------------------------------------------------------
+def test_masked_long_context_full_size(sa):
+    s = si.MASKED
+    q, k, v, mask, cleared = si.masked_inputs()
+    qd, kd, vd, md = q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(mask).to(DEV)
+    out, lse = sa.fwd(qd, kd, vd, causal=True, mask=md)
+    torch.cuda.synchronize()
+    N, H = s["N"], s["H"]
+    assert not torch.isnan(out).any()
+    # every all-masked row (the cleared ones and any naturally empty causal prefix row)
+    vis_any = np.zeros(N, bool)
+    tri_rows = np.nonzero(mask.any(axis=1))[0]
+    for i in tri_rows:
+        vis_any[i] = mask[i, : i + 1].any()
+    empty = np.nonzero(~vis_any)[0]
+    assert set(cleared.tolist()) <= set(empty.tolist())
+    o = out.reshape(N, H, -1)[torch.from_numpy(empty).to(DEV)]
+    l = lse.reshape(N, H)[torch.from_numpy(empty).to(DEV)]
+    assert bool((o == 0).all()) and bool((l == -math.inf).all())
+    assert bool(torch.isfinite(lse.reshape(N, H)[torch.from_numpy(np.nonzero(vis_any)[0]).to(DEV)]).all())
+    rows = _sample_rows(si.rng_for(87, 0), 1, N, H, 96, extra_rows=(int(empty[0]), 1, 16383))
+    ref, ref_lse = oracle.attn_dense(q, k, v, causal=True, mask=mask, rows=rows)
+    rt = torch.from_numpy(rows).to(DEV)
+    _compare(out.reshape(-1, s["D"])[rt], lse.reshape(-1)[rt], ref, ref_lse, "bf16", "masked")
+
+
+@pytest.mark.parametrize("D,BN", [(16, 32), (64, 64), (128, 64), (256, 64)])
+def test_mask_ragged_small(sa, D, BN):
+    """Arbitrary masks with ragged N (odd lengths, unaligned mask rows) against the oracle."""
+    rng = si.rng_for(88, D)
+    N = 203
+    q, k, v = (si.cast(x, "f16") for x in si.draw_qkv(rng, (1, N, 2, D), (1, N, 2, D)))
+    mask, _ = si.bernoulli_mask(rng, N, N, 3)
+    for causal in (False, True):
+        out, lse = sa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, mask=torch.from_numpy(mask).to(DEV), block_n=BN)
+        ref, ref_lse = oracle.attn_dense(q, k, v, causal=causal, mask=mask)
+        _compare(out.reshape(-1, D), lse.reshape(-1), ref, ref_lse, "f16", f"mask D={D} causal={causal}")
+
+
+# ---------------------------------------------------------------------------------------------
+# the combine on its own: static-P and runtime-P instantiations, every output dtype
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("P", [1, 2, 4, 8, 16, 37, 64, 65, 200, 256])
+@pytest.mark.parametrize("depth", [16, 64, 128, 256])
+def test_combine_against_oracle(sa, P, depth):
+    rng = np.random.default_rng(P * 1000 + depth)
+    rows, heads = 5, 3
+    o_p = rng.standard_normal((P, rows, heads, depth)).astype(np.float32)
+    l_p = (rng.standard_normal((P, rows, heads)) * 4).astype(np.float32)
+    l_p[rng.random((P, rows, heads)) < 0.2] = -np.inf
+    l_p[:, 0, 0] = -np.inf                           # one row-head with every partition empty
+    o_p[l_p == -np.inf] = 0.0
+    ref, G = oracle.combine_log2(o_p.reshape(P, rows * heads, depth).astype(np.float64),
+                                 l_p.reshape(P, -1).astype(np.float64))
+    for out_dtype, tol in ((torch.float32, 1e-5), (torch.bfloat16, 2e-2), (torch.float16, 5e-3)):
+        out, lse = sa.combine(torch.from_numpy(o_p).to(DEV), torch.from_numpy(l_p).to(DEV), out_dtype)
+        o = out.float().cpu().numpy().reshape(rows * heads, depth)
+        err = np.abs(o - ref).max()
+        assert err <= tol * max(1.0, np.abs(ref).max()), (out_dtype, err)
+        l = lse.cpu().numpy().reshape(-1).astype(np.float64)
+        fin = np.isfinite(G)
+        assert np.all(l[~fin] == -np.inf) and np.all(o[~fin] == 0)
+        np.testing.assert_allclose(l[fin], G[fin] * math.log(2.0), rtol=1e-5, atol=1e-5)
+
+
+# ---------------------------------------------------------------------------------------------
+# reject paths with real buffers: nothing is written
+# ---------------------------------------------------------------------------------------------
+def test_reject_paths_write_nothing(sa):
+    q = torch.randn(1, 64, 2, 64, device=DEV).to(torch.bfloat16)
+    out = torch.full_like(q, 7.0)
+    o_p = torch.full((4, 64, 2, 64), 7.0, device=DEV)
+    l_p = torch.full((4, 64, 2), 7.0, device=DEV)
+    with pytest.raises(sa.AttnError):
+        sa.attn_fwd_splitk(q, q[:, :32], q[:, :32], 4, o_p, l_p, causal=True)   # rectangular causal
+    with pytest.raises(sa.AttnError):
+        sa.attn_fwd_splitk(q, q, q, 0, o_p, l_p)
+    with pytest.raises(sa.AttnError):
+        sa.attn_fwd(q, q, q, out, block_n=48)
+    q48 = torch.zeros(1, 64, 2, 48, device=DEV, dtype=torch.bfloat16)
+    with pytest.raises(sa.AttnError):
+        sa.attn_fwd(q48, q48, q48, torch.zeros_like(q48))
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()) and bool((o_p == 7.0).all()) and bool((l_p == 7.0).all())
