@@ -100,8 +100,9 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "combine"], default=None,
-                    help="time a single kernel (for profiler runs); the JSON line is still printed")
+    ap.add_argument("--only", choices=["prefill", "decode", "combine", "copy"], default=None,
+                    help="time a single kernel (for profiler runs); 'copy' times a plain 1 GiB device "
+                         "copy, the calibration for the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -113,6 +114,13 @@ def main():
     import streaming_online_softmax_amd as sa
 
     dev = torch.device("cuda:0")
+    if args.only == "copy":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        _, ms = timed_events([lambda: dst.copy_(src)], args.steps, args.warmup)
+        print(json.dumps({"calibration": "device copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                          "ms": ms[0], "GB/s": 2 * (1 << 30) / (ms[0] * 1e-3) / 1e9}), flush=True)
+        return
     # ---- inputs (seeded, synthetic, resident in HBM before timing) -----------------------
     sp = si.PREFILL
     qc, kc, vc = si.prefill_inputs()

@@ -43,22 +43,29 @@ __device__ __forceinline__ int key_perm(int i) {
   return ((b >> 1) << 4) + (h << 3) + ((b & 1) << 2) + (i & 3);
 }
 
+// Lazy rescale threshold (log2 units): the reference maximum m is raised only when some row of
+// the wave sees a score more than TAU above it, so weights stay <= 2^TAU and the O rescale is
+// skipped on most tiles.  O / l and m + log2(l) do not depend on which reference is used.
+constexpr float kTau = 8.0f;
+
 template <typename T, int D, int BN, bool MASK, bool SPLIT>
 __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdParams p) {
   using E = elem<T>;
   constexpr int DP = D < 32 ? 32 : D;   // rows of O^T (padded to one 32-row MFMA tile)
-  constexpr int KS = D + 8;             // LDS row stride of K (elements), 16 B of padding
-  constexpr int VS = DP + 8;            // LDS row stride of V
+  constexpr int RB = D * 2;             // bytes per K / V row in LDS (unpadded)
+  constexpr int CH = D / 8;             // 16-byte chunks per row
+  constexpr int SWZ = CH < 16 ? CH - 1 : 15;   // chunk index XOR (row & SWZ): conflict-free reads
+  constexpr int TILE = BN * RB;         // bytes of one K (or V) tile
+  constexpr int NT = TILE / 1024;       // 1 KiB wave-instructions per tile per tensor
+  constexpr int RPI = 1024 / RB;        // rows covered by one wave-instruction
   constexpr int KSTEPS = D / 16;        // k-steps of S^T = K Q^T
   constexpr int MT = BN / 32;           // 32-key blocks per tile
   constexpr int DT = DP / 32;           // 32-row tiles of O^T
   constexpr int PK = BN / 16;           // k-steps of O^T = V^T P^T
-  constexpr int CH = D / 8;             // 16-byte chunks per K/V row
-  constexpr int CHUNKS = BN * CH;       // chunks per K (and per V) tile
-  constexpr int CPT = (CHUNKS + 255) / 256;
+  static_assert(TILE % 1024 == 0, "tile must be a whole number of 1 KiB wave loads");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * VS];
+  // two stages of (K, V)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * 2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -88,13 +95,30 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
   const uint16_t* kbase = (const uint16_t*)p.k + ((int64_t)b * p.Nkv * p.H + h) * D;
   const uint16_t* vbase = (const uint16_t*)p.v + ((int64_t)b * p.Nkv * p.H + h) * D;
 
-  // D < 32: O^T rows D..31 read zero V columns (set once; staging never writes them).
-  if constexpr (DP != D) {
-    for (int i = tid; i < BN * (VS - D); i += 256) {
-      int r = i / (VS - D), c = D + i % (VS - D);
-      Vs[r * VS + c] = 0;
+  // ---- direct global -> LDS staging.  Wave-instruction j of a tile fills LDS bytes
+  //      [1024 j, 1024 j + 1024): lane l lands at row j*RPI + l/CH, physical chunk l%CH, which
+  //      holds logical chunk (l%CH) ^ (row & SWZ) of that key row.
+  const int ld_row_in = lane / CH;
+  const int ld_pc = lane % CH;
+  auto issue_tile = [&](int t, int stage) {
+    const int k0 = kbeg + t * BN;
+    uint8_t* kdst = lds + stage * 2 * TILE;
+    uint8_t* vdst = kdst + TILE;
+    const bool tail = k0 + BN > p.Nkv;
+    constexpr int PER_WAVE = (NT + kWaves - 1) / kWaves;
+#pragma unroll
+    for (int jj = 0; jj < PER_WAVE; ++jj) {
+      const int j = jj * kWaves + wave;
+      if (NT % kWaves != 0 && j >= NT) break;
+      const int row = j * RPI + ld_row_in;
+      const int c = ld_pc ^ (row & SWZ);
+      int key = k0 + row;
+      if (tail) key = key < p.Nkv ? key : p.Nkv - 1;   // rows past the end are masked; read a valid row
+      const int64_t off = (int64_t)key * row_stride + 8 * c;
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + off), (__attribute__((address_space(3))) void*)(kdst + j * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + off), (__attribute__((address_space(3))) void*)(vdst + j * 1024), 16, 0, 0);
     }
-  }
+  };
 
   // ---- Q^T as the B operand of S^T = K Q^T: lane holds Q[qi][16*ks + 8*(lane/32) .. +8]
   u32x4 qf[KSTEPS];
@@ -109,74 +133,72 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
   }
 
   // ---- running state (one query per lane; replicated in lanes l and l^32)
-  float m_run = kNegInf;   // running max of log2-unit scores
+  float m_run = kNegInf;   // reference maximum of log2-unit scores
   float l_run = 0.f;       // this lane's partial denominator (its 16 keys of every 32)
   f32x16 oacc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) oacc[i] = f32x16{};
 
   const float c = p.scale_log2;   // log2(e) / sqrt(D)
-
-  // register staging of the next tile (prefetched while the current one is computed)
-  u32x4 kreg[CPT], vreg[CPT];
-  auto load_tile = [&](int t) {
-    const int k0 = kbeg + t * BN;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cidx = tid + i * 256;
-      if (CHUNKS % 256 == 0 || cidx < CHUNKS) {
-        const int r = cidx / CH, cc = cidx % CH;
-        int key = k0 + r;
-        key = key < p.Nkv ? key : p.Nkv - 1;   // rows past the end are masked; read a valid row
-        kreg[i] = ld16(kbase + (int64_t)key * row_stride + cc * 8);
-        vreg[i] = ld16(vbase + (int64_t)key * row_stride + cc * 8);
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cidx = tid + i * 256;
-      if (CHUNKS % 256 == 0 || cidx < CHUNKS) {
-        const int r = cidx / CH, cc = cidx % CH;
-        *reinterpret_cast<u32x4*>(&Ks[r * KS + cc * 8]) = kreg[i];
-        *reinterpret_cast<u32x4*>(&Vs[r * VS + cc * 8]) = vreg[i];
-      }
-    }
-  };
-
   const bool wave_has_rows = q0 < p.Nq;
-  if (ntiles > 0) load_tile(0);
+  const int kl = 8 * (lane >> 5);
+
+  // per-lane LDS byte offsets of the operand reads (stage-relative)
+  int koff[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) koff[mt] = (mt * 32 + key_perm(lane & 31)) * RB;
+  const int krow_swz = key_perm(lane & 31) & SWZ;   // (mt*32 + r) & SWZ == r & SWZ for SWZ < 32
+  const int g = lane >> 4, li = lane & 15;
+  const int jrow = li >> 2, tq = li & 3;
+  const bool dpad = (D < 32) && ((g & 1) != 0);    // O^T rows D..31 for D = 16: zero operand
+
+  if (ntiles > 0) issue_tile(0, 0);
 
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = kbeg + t * BN;
-    __syncthreads();          // every wave is done reading the previous tile
-    store_tile();
+    const int stage = t & 1;
+    // tile t resident for every wave (its LDS-DMA loads are counted by vmcnt, which the
+    // barrier's own fence does not wait for); every wave done with tile t-1's stage
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);
+    if (t + 1 < ntiles) issue_tile(t + 1, stage ^ 1);
 
     // wave-uniform decisions for this tile
     const bool future = p.causal && (k0 > q0 + kRowsPerWave - 1);   // no key visible to any row
     if (!wave_has_rows || future) continue;
     const bool need_tail = (k0 + BN > kend);
     const bool need_causal = p.causal && (k0 + BN - 1 > q0);
+    const uint8_t* ks_base = lds + stage * 2 * TILE;
+    const uint8_t* vs_base = ks_base + TILE;
 
-    // ---- S^T = K Q^T  (MT blocks of 32 keys x 32 queries)
+    // ---- S^T = K Q^T  (MT blocks of 32 keys x 32 queries).  The K fragments are read in
+    //      batches of up to 16 (64 VGPRs) before the products that consume them, so one LDS
+    //      latency is exposed per batch instead of one per product.
     f32x16 sacc[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      sacc[mt] = f32x16{};
-      const uint16_t* krow = &Ks[(mt * 32 + key_perm(lane & 31)) * KS + 8 * (lane >> 5)];
+    for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
+    constexpr int NF = MT * KSTEPS;                  // fragments per tile, ordered (mt, ks)
+    constexpr int FB = (D >= 256 ? 8 : 16) < NF ? (D >= 256 ? 8 : 16) : NF;   // fragments per batch
+    static_assert(NF % FB == 0, "fragment batches must tile the key block");
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        u32x4 a = *reinterpret_cast<const u32x4*>(krow + 16 * ks);
-        sacc[mt] = E::mfma32(a, qf[ks], sacc[mt]);
+    for (int f0 = 0; f0 < NF; f0 += FB) {
+      u32x4 kf[FB];
+#pragma unroll
+      for (int f = 0; f < FB; ++f) {
+        const int mt = (f0 + f) / KSTEPS, ks = (f0 + f) % KSTEPS;
+        const int cidx = (2 * ks + (lane >> 5)) ^ krow_swz;
+        kf[f] = *reinterpret_cast<const u32x4*>(ks_base + koff[mt] + 16 * cidx);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int f = 0; f < FB; ++f) {
+        const int mt = (f0 + f) / KSTEPS, ks = (f0 + f) % KSTEPS;
+        sacc[mt] = E::mfma32(kf[f], qf[ks], sacc[mt]);
       }
     }
 
     // ---- masks (select to -inf).  Register r of block mt holds key
     //      k0 + 32*mt + 16*(r/8) + 8*(lane/32) + r%8 for query qi.
-    const int kl = 8 * (lane >> 5);
     if (need_tail || need_causal) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -216,17 +238,24 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
         }
     }
 
-    // ---- online softmax update (one query per lane)
+    // ---- online softmax update (one query per lane), lazy rescale by wave vote
     float mx = kNegInf;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
-    mx = xor32_max(mx);                              // the other 16 keys of each block
-    const float m_new = fmaxf(m_run, mx * c);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;   // all-masked so far: no -inf - -inf
-    const float alpha = fast_exp2(m_run - m_use);           // 0 from the empty state
-    m_run = m_new;
+    mx = xor32_max(mx) * c;                          // the other 16 keys of each block
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {   // wave-uniform
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);  // 0 from the empty state; m_new is finite here
+                                                      // for rows that saw a key, else m_run = -inf
+      const float alpha_s = (m_new == kNegInf) ? 1.f : alpha;
+      l_run *= alpha_s;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha_s;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;   // all-masked so far: no -inf - -inf
 
     float psum = 0.f;
     u32x4 pf[PK];
@@ -243,30 +272,37 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
         pf[2 * mt + hf] = u32x4{E::pack2(pv[0], pv[1]), E::pack2(pv[2], pv[3]),
                                 E::pack2(pv[4], pv[5]), E::pack2(pv[6], pv[7])};
       }
-    l_run = alpha * l_run + psum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    l_run += psum;
 
     // ---- O^T += V^T P^T.  A operand (V^T, 32 d-rows x 16 keys) through transposing LDS reads:
     //      16-lane group g covers d = 32*dt + 16*(g%2) .. +16 and keys 16*kk + 8*(g/2) + {0..3},
     //      {4..7}; lane 4*j + tq of the group addresses key row (.. + j), d chunk 4*tq.
-    {
-      const int g = lane >> 4, li = lane & 15;
-      const int jrow = li >> 2, tq = li & 3;
+    constexpr int VB = (PK * DT <= 16) ? PK : (DT < 8 ? 16 / DT : 1);   // key steps per batch
 #pragma unroll
-      for (int kk = 0; kk < PK; ++kk) {
-        const int krow = 16 * kk + 8 * (g >> 1) + jrow;
+    for (int kb = 0; kb < PK; kb += VB) {
+      u32x4 va[VB][DT];
+#pragma unroll
+      for (int k2 = 0; k2 < VB; ++k2) {
+        const int vrow = 16 * (kb + k2) + 8 * (g >> 1) + jrow;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int dcol = 32 * dt + 16 * (g & 1) + 4 * tq;
+          const int d = 32 * dt + 16 * (g & 1) + 4 * tq;
+          const int cidx = (d / 8) % CH;
           typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-          i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&Vs[krow * VS + dcol]);
-          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&Vs[(krow + 4) * VS + dcol]);
+          const uint8_t* a0 = vs_base + vrow * RB + 16 * (cidx ^ (vrow & SWZ)) + 8 * (tq & 1);
+          const uint8_t* a1 = vs_base + (vrow + 4) * RB + 16 * (cidx ^ ((vrow + 4) & SWZ)) + 8 * (tq & 1);
+          i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
+          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a1);
           u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          u32x4 a = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-          oacc[dt] = E::mfma32(a, pf[kk], oacc[dt]);
+          va[k2][dt] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+          if (dpad) va[k2][dt] = u32x4{0, 0, 0, 0};
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k2 = 0; k2 < VB; ++k2)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] = E::mfma32(va[k2][dt], pf[kb + k2], oacc[dt]);
     }
   }
 

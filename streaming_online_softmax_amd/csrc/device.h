@@ -7,6 +7,8 @@
 //   C (32 x 32):  lane l, register r holds C[(r / 4) * 8 + (l / 32) * 4 + (r % 4)][l % 32]
 // ds_read_b64_tr_b16 (per 16-lane group): lane i receives, for j = 0..3, element (i % 4) of the
 // 8-byte chunk addressed by lane 4 * j + i / 4 of its group.
+// global_load_lds_dwordx4 writes lane l's 16 bytes at LDS base + 16 * l (a wave-instruction
+// fills 1 KiB contiguously); its immediate offset is added to both addresses.
 // v_permlane32_swap(x, x) returns (x_lo32 | x_lo32, x_hi32 | x_hi32) as a pair, so combining the
 // pair gives the xor-32 reduction in every lane; v_permlane16_swap does the same for xor 16.
 #pragma once
@@ -22,6 +24,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -29,7 +34,9 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 // ------------------------------------------------------------------------------------------
 // Element types.  Storage is raw 16-bit words; conversions round to nearest even (the
-// hardware conversions v_cvt_pk_bf16_f32 and v_cvt_f16_f32 under the default rounding mode).
+// hardware conversions v_cvt_pk_bf16_f32 and v_cvt_pk_f16_f32 under the default rounding mode,
+// checked on gfx950 against an independent RNE reference including ties, subnormals, signed
+// zero, infinities and overflow).
 // ------------------------------------------------------------------------------------------
 struct bf16_t { uint16_t bits; };
 struct f16_t { uint16_t bits; };
@@ -38,9 +45,9 @@ template <typename T> struct elem;
 template <> struct elem<bf16_t> {
   typedef bf16x8 vec8;
   static __device__ __forceinline__ float to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+  // one v_cvt_pk_bf16_f32: lo in bits 15:0, hi in bits 31:16
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
   }
   static __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -49,9 +56,9 @@ template <> struct elem<bf16_t> {
 template <> struct elem<f16_t> {
   typedef f16x8 vec8;
   static __device__ __forceinline__ float to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+  // one v_cvt_pk_f16_f32 (round to nearest even, subnormals kept)
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
   }
   static __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
