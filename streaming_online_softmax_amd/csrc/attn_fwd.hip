@@ -48,13 +48,22 @@ __device__ __forceinline__ int key_perm(int i) {
 // skipped on most tiles.  O / l and m + log2(l) do not depend on which reference is used.
 constexpr float kTau = 8.0f;
 
+// LDS chunk swizzles (16-byte chunk index XOR, per key row).
+template <int SWZ>
+__device__ __forceinline__ int k_swz(int row) { return row & SWZ; }
+template <int RPB, int BITS>
+__device__ __forceinline__ int v_swz(int row) { return BITS ? 4 * ((row / RPB) & BITS) : 0; }
+
 template <typename T, int D, int BN, bool MASK, bool SPLIT>
 __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdParams p) {
   using E = elem<T>;
   constexpr int DP = D < 32 ? 32 : D;   // rows of O^T (padded to one 32-row MFMA tile)
   constexpr int RB = D * 2;             // bytes per K / V row in LDS (unpadded)
   constexpr int CH = D / 8;             // 16-byte chunks per row
-  constexpr int SWZ = CH < 16 ? CH - 1 : 15;   // chunk index XOR (row & SWZ): conflict-free reads
+  constexpr int SWZ = CH < 16 ? CH - 1 : 15;   // K chunk index XOR (row & SWZ): conflict-free b128 reads
+  // V chunk XOR: the four key rows one transposing read touches must fall on distinct banks
+  constexpr int RPB = RB >= 256 ? 1 : 256 / RB;            // key rows per 256-byte bank line
+  constexpr int VSWZ_BITS = CH >= 16 ? 3 : (CH >= 8 ? 1 : 0);
   constexpr int TILE = BN * RB;         // bytes of one K (or V) tile
   constexpr int NT = TILE / 1024;       // 1 KiB wave-instructions per tile per tensor
   constexpr int RPI = 1024 / RB;        // rows covered by one wave-instruction
@@ -71,12 +80,16 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  // ---- block coordinates: h fastest, then b, then partition, then query block (longest first)
+  // ---- block coordinates.  Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8),
+  //      so the linear order is remapped to give each XCD a contiguous run of blocks: the query
+  //      blocks of one (head, batch) then run together on one XCD and share its L2 for K and V.
   int bid = blockIdx.x;
+  if (gridDim.x % 8 == 0) bid = (bid % 8) * (gridDim.x / 8) + bid / 8;
+  const int qb_idx = bid % p.n_qblocks; bid /= p.n_qblocks;
   const int h = bid % p.H; bid /= p.H;
   const int b = bid % p.B; bid /= p.B;
-  const int part = bid % p.P; bid /= p.P;
-  const int qb = p.causal ? (p.n_qblocks - 1 - bid) : bid;
+  const int part = bid;
+  const int qb = p.causal ? (p.n_qblocks - 1 - qb_idx) : qb_idx;   // causal: longest first
 
   const int q_block0 = qb * kBlockM;
   const int q0 = q_block0 + wave * kRowsPerWave;   // first query row of this wave
@@ -95,28 +108,43 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
   const uint16_t* kbase = (const uint16_t*)p.k + ((int64_t)b * p.Nkv * p.H + h) * D;
   const uint16_t* vbase = (const uint16_t*)p.v + ((int64_t)b * p.Nkv * p.H + h) * D;
 
-  // ---- direct global -> LDS staging.  Wave-instruction j of a tile fills LDS bytes
-  //      [1024 j, 1024 j + 1024): lane l lands at row j*RPI + l/CH, physical chunk l%CH, which
-  //      holds logical chunk (l%CH) ^ (row & SWZ) of that key row.
+  // ---- direct global -> LDS staging (buffer_load ... lds).  Wave-instruction j of a tile fills
+  //      LDS bytes [1024 j, 1024 j + 1024): lane l lands at row j*RPI + l/CH, physical chunk
+  //      l%CH, which holds logical chunk (l%CH) ^ swizzle(row) of that key row.  The per-lane
+  //      byte offsets inside a tile are fixed; each tile only moves the scalar base.
+  constexpr int PER_WAVE = (NT + kWaves - 1) / kWaves;
   const int ld_row_in = lane / CH;
   const int ld_pc = lane % CH;
+  uint32_t kvo[PER_WAVE], vvo[PER_WAVE];
+  int ld_row[PER_WAVE];
+#pragma unroll
+  for (int jj = 0; jj < PER_WAVE; ++jj) {
+    const int row = (jj * kWaves + wave) * RPI + ld_row_in;
+    ld_row[jj] = row;
+    kvo[jj] = (uint32_t)(((int64_t)row * row_stride + 8 * (ld_pc ^ k_swz<SWZ>(row))) * 2);
+    vvo[jj] = (uint32_t)(((int64_t)row * row_stride + 8 * (ld_pc ^ v_swz<RPB, VSWZ_BITS>(row))) * 2);
+  }
+  const uint32_t tile_bytes = (uint32_t)((int64_t)BN * row_stride * 2);
   auto issue_tile = [&](int t, int stage) {
     const int k0 = kbeg + t * BN;
     uint8_t* kdst = lds + stage * 2 * TILE;
     uint8_t* vdst = kdst + TILE;
+    __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)k0 * row_stride), 0, tile_bytes, 0x00020000);
+    __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)k0 * row_stride), 0, tile_bytes, 0x00020000);
     const bool tail = k0 + BN > p.Nkv;
-    constexpr int PER_WAVE = (NT + kWaves - 1) / kWaves;
 #pragma unroll
     for (int jj = 0; jj < PER_WAVE; ++jj) {
       const int j = jj * kWaves + wave;
       if (NT % kWaves != 0 && j >= NT) break;
-      const int row = j * RPI + ld_row_in;
-      const int c = ld_pc ^ (row & SWZ);
-      int key = k0 + row;
-      if (tail) key = key < p.Nkv ? key : p.Nkv - 1;   // rows past the end are masked; read a valid row
-      const int64_t off = (int64_t)key * row_stride + 8 * c;
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + off), (__attribute__((address_space(3))) void*)(kdst + j * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vbase + off), (__attribute__((address_space(3))) void*)(vdst + j * 1024), 16, 0, 0);
+      uint32_t ko = kvo[jj], vo = vvo[jj];
+      if (tail) {   // rows past the end are masked; read the last valid row instead
+        const int row = ld_row[jj];
+        const int rr = (k0 + row < p.Nkv ? k0 + row : p.Nkv - 1) - k0;
+        ko = (uint32_t)(((int64_t)rr * row_stride + 8 * (ld_pc ^ k_swz<SWZ>(row))) * 2);
+        vo = (uint32_t)(((int64_t)rr * row_stride + 8 * (ld_pc ^ v_swz<RPB, VSWZ_BITS>(row))) * 2);
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kdst + j * 1024), 16, ko, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + j * 1024), 16, vo, 0, 0, 0);
     }
   };
 
@@ -147,7 +175,7 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
   int koff[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) koff[mt] = (mt * 32 + key_perm(lane & 31)) * RB;
-  const int krow_swz = key_perm(lane & 31) & SWZ;   // (mt*32 + r) & SWZ == r & SWZ for SWZ < 32
+  const int krow_swz = k_swz<SWZ>(key_perm(lane & 31));   // equal for mt*32 + r: SWZ < 32
   const int g = lane >> 4, li = lane & 15;
   const int jrow = li >> 2, tq = li & 3;
   const bool dpad = (D < 32) && ((g & 1) != 0);    // O^T rows D..31 for D = 16: zero operand
@@ -289,8 +317,8 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
           const int d = 32 * dt + 16 * (g & 1) + 4 * tq;
           const int cidx = (d / 8) % CH;
           typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-          const uint8_t* a0 = vs_base + vrow * RB + 16 * (cidx ^ (vrow & SWZ)) + 8 * (tq & 1);
-          const uint8_t* a1 = vs_base + (vrow + 4) * RB + 16 * (cidx ^ ((vrow + 4) & SWZ)) + 8 * (tq & 1);
+          const uint8_t* a0 = vs_base + vrow * RB + 16 * (cidx ^ v_swz<RPB, VSWZ_BITS>(vrow)) + 8 * (tq & 1);
+          const uint8_t* a1 = vs_base + (vrow + 4) * RB + 16 * (cidx ^ v_swz<RPB, VSWZ_BITS>(vrow + 4)) + 8 * (tq & 1);
           i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
           i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a1);
           u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
