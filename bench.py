@@ -13,6 +13,7 @@ workspace too large for the caches.  Every per-kernel time comes from HIP events
 stream the kernels are launched on, over the whole timed region.  Rank 0 prints one JSON line.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -45,6 +46,38 @@ def decode_bytes(B, H, Nkv, D, P):
 
 def combine_bytes(P, RH, D, out_elem=2):
     return P * RH * (D + 1) * 4 + RH * D * out_elem + RH * 4
+
+
+KERNEL_SOURCES = ("attn_fwd.hip", "device.h", "launch.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_prefill_B4H32N4096D128_hbm_traffic.txt")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "streaming_online_softmax_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the prefill kernel from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter on a 1 GiB device copy), or
+    None when that summary was taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def timed_events(fn_list, steps, warmup):
@@ -217,7 +250,8 @@ def main():
     }
     if value is not None:
         line["roofline"] = {"bound": "mfma", "achieved": value, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                            "frac": value / PEAK_BF16_TFLOPS, "traffic": None,
+                            "frac": value / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
+                            "traffic_unit": "bytes per launch (HBM, counter-measured)",
                             "kernel": "attn_fwd_kernel<bf16, D=128, BN=64>",
                             "work_per_launch": f"{fl:.4e} FLOP (4*D per causal pair)"}
     line.update(extra)

@@ -2,7 +2,7 @@
 
 The binding only marshals arguments: every step of the computation runs in the HIP kernels of
 libattn.so (built from ``csrc/`` by ``build.py``).  torch supplies device memory and streams.
-If the library has not been built, importing the binding raises -- there is no fallback.
+If the library has not been built, the first call raises -- there is no fallback.
 
 Entry points (same names as the C ABI in include/attn.h):
     attn_fwd(q, k, v, out, lse=None, causal=False, mask=None, block_n=0, stream=None)
@@ -43,6 +43,17 @@ class FwdArgs(ctypes.Structure):
                 ("causal", ctypes.c_int), ("dtype", ctypes.c_int), ("block_n", ctypes.c_int)]
 
 
+_LIB = None
+
+
+def lib():
+    """The loaded libattn.so (ctypes).  Raises if it is missing or fails to load."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run `python -m streaming_online_softmax_amd.build`")
@@ -61,8 +72,6 @@ def _load():
     return L
 
 
-lib = _load()
-
 
 def declared_symbols():
     """Function names the public header declares."""
@@ -72,11 +81,11 @@ def declared_symbols():
 
 
 def attn_last_error():
-    return lib.attn_last_error().decode()
+    return lib().attn_last_error().decode()
 
 
 def attn_abi_version():
-    return int(lib.attn_abi_version())
+    return int(lib().attn_abi_version())
 
 
 def _check(rc):
@@ -111,14 +120,14 @@ def attn_fwd(q, k, v, out, lse=None, causal=False, mask=None, block_n=0, stream=
     B, N, H, D = q.shape
     a = FwdArgs(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(mask),
                 B, H, N, D, int(causal), _dtype_code(q), int(block_n))
-    _check(lib.attn_fwd_ex(ctypes.byref(a), _stream(stream)))
+    _check(lib().attn_fwd_ex(ctypes.byref(a), _stream(stream)))
 
 
 def attn_fwd_splitk(q, k, v, P, o_partial, lse_partial, out=None, lse=None, causal=False, mask=None,
                     stream=None):
     B, Nq, H, D = q.shape
     Nkv = k.shape[1]
-    _check(lib.attn_fwd_splitk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nkv, D,
+    _check(lib().attn_fwd_splitk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nkv, D,
                                int(causal), _ptr(mask), int(P), _ptr(o_partial), _ptr(lse_partial),
                                _dtype_code(q), _stream(stream)))
 
@@ -128,7 +137,7 @@ def attn_combine(o_partial, lse_partial, out, lse_out=None, stream=None):
     depth = o_partial.shape[-1]
     heads = o_partial.shape[-2]
     rows = o_partial[0].numel() // (heads * depth)
-    _check(lib.attn_combine(_ptr(o_partial), _ptr(lse_partial), _ptr(out), _ptr(lse_out), int(P),
+    _check(lib().attn_combine(_ptr(o_partial), _ptr(lse_partial), _ptr(out), _ptr(lse_out), int(P),
                             rows, heads, depth, _dtype_code(out), _stream(stream)))
 
 

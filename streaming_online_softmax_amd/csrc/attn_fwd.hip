@@ -29,6 +29,8 @@
 #include "device.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace attn {
 
 constexpr int kWaves = 4;
@@ -70,7 +72,6 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
   constexpr int KSTEPS = D / 16;        // k-steps of S^T = K Q^T
   constexpr int MT = BN / 32;           // 32-key blocks per tile
   constexpr int DT = DP / 32;           // 32-row tiles of O^T
-  constexpr int PK = BN / 16;           // k-steps of O^T = V^T P^T
   static_assert(TILE % 1024 == 0, "tile must be a whole number of 1 KiB wave loads");
 
   // two stages of (K, V)
@@ -113,38 +114,51 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
   //      l%CH, which holds logical chunk (l%CH) ^ swizzle(row) of that key row.  The per-lane
   //      byte offsets inside a tile are fixed; each tile only moves the scalar base.
   constexpr int PER_WAVE = (NT + kWaves - 1) / kWaves;
+  // Row of instruction jj = (jj*4 + wave)*RPI + lane/CH.  When 4*RPI is a multiple of 16 (D <= 128)
+  // neither swizzle depends on jj, so one per-lane offset serves every instruction and the jj
+  // part goes into the scalar offset.
+  constexpr bool ONE_OFS = (4 * RPI) % 16 == 0;
   const int ld_row_in = lane / CH;
   const int ld_pc = lane % CH;
-  uint32_t kvo[PER_WAVE], vvo[PER_WAVE];
-  int ld_row[PER_WAVE];
-#pragma unroll
-  for (int jj = 0; jj < PER_WAVE; ++jj) {
-    const int row = (jj * kWaves + wave) * RPI + ld_row_in;
-    ld_row[jj] = row;
-    kvo[jj] = (uint32_t)(((int64_t)row * row_stride + 8 * (ld_pc ^ k_swz<SWZ>(row))) * 2);
-    vvo[jj] = (uint32_t)(((int64_t)row * row_stride + 8 * (ld_pc ^ v_swz<RPB, VSWZ_BITS>(row))) * 2);
-  }
+  const int row0 = wave * RPI + ld_row_in;
+  const uint32_t kvo0 = (uint32_t)(((int64_t)row0 * row_stride + 8 * (ld_pc ^ k_swz<SWZ>(row0))) * 2);
+  const uint32_t vvo0 = (uint32_t)(((int64_t)row0 * row_stride + 8 * (ld_pc ^ v_swz<RPB, VSWZ_BITS>(row0))) * 2);
+  const uint32_t jj_bytes = (uint32_t)((int64_t)kWaves * RPI * row_stride * 2);   // scalar step per jj
   const uint32_t tile_bytes = (uint32_t)((int64_t)BN * row_stride * 2);
   auto issue_tile = [&](int t, int stage) {
     const int k0 = kbeg + t * BN;
-    uint8_t* kdst = lds + stage * 2 * TILE;
+    // the LDS destination goes to M0, which must be provably wave-uniform
+    uint8_t* kdst = lds + __builtin_amdgcn_readfirstlane(stage * 2 * TILE + wave * 1024);
     uint8_t* vdst = kdst + TILE;
     __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)k0 * row_stride), 0, tile_bytes, 0x00020000);
     __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)k0 * row_stride), 0, tile_bytes, 0x00020000);
-    const bool tail = k0 + BN > p.Nkv;
+    if (k0 + BN <= p.Nkv) {
 #pragma unroll
-    for (int jj = 0; jj < PER_WAVE; ++jj) {
-      const int j = jj * kWaves + wave;
-      if (NT % kWaves != 0 && j >= NT) break;
-      uint32_t ko = kvo[jj], vo = vvo[jj];
-      if (tail) {   // rows past the end are masked; read the last valid row instead
-        const int row = ld_row[jj];
-        const int rr = (k0 + row < p.Nkv ? k0 + row : p.Nkv - 1) - k0;
-        ko = (uint32_t)(((int64_t)rr * row_stride + 8 * (ld_pc ^ k_swz<SWZ>(row))) * 2);
-        vo = (uint32_t)(((int64_t)rr * row_stride + 8 * (ld_pc ^ v_swz<RPB, VSWZ_BITS>(row))) * 2);
+      for (int jj = 0; jj < PER_WAVE; ++jj) {
+        const int j = jj * kWaves + wave;
+        if (NT % kWaves != 0 && j >= NT) break;
+        uint32_t ko = kvo0, vo = vvo0, so = jj * jj_bytes;
+        if constexpr (!ONE_OFS) {   // the swizzles depend on the instruction: per-lane offsets
+          const int row = j * RPI + ld_row_in;
+          ko = (uint32_t)(((int64_t)row * row_stride + 8 * (ld_pc ^ k_swz<SWZ>(row))) * 2);
+          vo = (uint32_t)(((int64_t)row * row_stride + 8 * (ld_pc ^ v_swz<RPB, VSWZ_BITS>(row))) * 2);
+          so = 0;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kdst + jj * kWaves * 1024), 16, ko, so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + jj * kWaves * 1024), 16, vo, so, 0, 0);
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kdst + j * 1024), 16, ko, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + j * 1024), 16, vo, 0, 0, 0);
+    } else {   // last tile: rows past the end are masked; read the last valid row instead
+#pragma unroll
+      for (int jj = 0; jj < PER_WAVE; ++jj) {
+        const int j = jj * kWaves + wave;
+        if (NT % kWaves != 0 && j >= NT) break;
+        const int row = j * RPI + ld_row_in;
+        const int rr = (k0 + row < p.Nkv ? k0 + row : p.Nkv - 1) - k0;
+        const uint32_t ko = (uint32_t)(((int64_t)rr * row_stride + 8 * (ld_pc ^ k_swz<SWZ>(row))) * 2);
+        const uint32_t vo = (uint32_t)(((int64_t)rr * row_stride + 8 * (ld_pc ^ v_swz<RPB, VSWZ_BITS>(row))) * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kdst + jj * kWaves * 1024), 16, ko, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + jj * kWaves * 1024), 16, vo, 0, 0, 0);
+      }
     }
   };
 
@@ -199,49 +213,61 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
     const uint8_t* ks_base = lds + stage * 2 * TILE;
     const uint8_t* vs_base = ks_base + TILE;
 
-    // ---- S^T = K Q^T  (MT blocks of 32 keys x 32 queries).  The K fragments are read in
-    //      batches of up to 16 (64 VGPRs) before the products that consume them, so one LDS
-    //      latency is exposed per batch instead of one per product.
-    f32x16 sacc[MT];
+    auto read_k = [&](int mt, u32x4 (&kf)[KSTEPS]) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
-    constexpr int NF = MT * KSTEPS;                  // fragments per tile, ordered (mt, ks)
-    constexpr int FB = (D >= 256 ? 8 : 16) < NF ? (D >= 256 ? 8 : 16) : NF;   // fragments per batch
-    static_assert(NF % FB == 0, "fragment batches must tile the key block");
-#pragma unroll
-    for (int f0 = 0; f0 < NF; f0 += FB) {
-      u32x4 kf[FB];
-#pragma unroll
-      for (int f = 0; f < FB; ++f) {
-        const int mt = (f0 + f) / KSTEPS, ks = (f0 + f) % KSTEPS;
+      for (int ks = 0; ks < KSTEPS; ++ks) {
         const int cidx = (2 * ks + (lane >> 5)) ^ krow_swz;
-        kf[f] = *reinterpret_cast<const u32x4*>(ks_base + koff[mt] + 16 * cidx);
+        kf[ks] = *reinterpret_cast<const u32x4*>(ks_base + koff[mt] + 16 * cidx);
       }
-      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto qk = [&](const u32x4 (&kf)[KSTEPS]) {
+      f32x16 acc = f32x16{};
 #pragma unroll
-      for (int f = 0; f < FB; ++f) {
-        const int mt = (f0 + f) / KSTEPS, ks = (f0 + f) % KSTEPS;
-        sacc[mt] = E::mfma32(kf[f], qf[ks], sacc[mt]);
+      for (int ks = 0; ks < KSTEPS; ++ks) acc = E::mfma32(kf[ks], qf[ks], acc);
+      return acc;
+    };
+    // V^T fragments of the two 16-key steps of block mt: 16-lane group g covers
+    // d = 32*dt + 16*(g%2) .. +16 and keys 16*kk + 8*(g/2) + {0..3}, {4..7}; lane 4*j + tq of the
+    // group addresses key row (.. + j), d chunk 4*tq.
+    auto read_v = [&](int mt, u32x4 (&va)[2][DT]) {
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int vrow = 16 * (2 * mt + k2) + 8 * (g >> 1) + jrow;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int d = 32 * dt + 16 * (g & 1) + 4 * tq;
+          const int cidx = (d / 8) % CH;
+          typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+          const uint8_t* a0 = vs_base + vrow * RB + 16 * (cidx ^ v_swz<RPB, VSWZ_BITS>(vrow)) + 8 * (tq & 1);
+          const uint8_t* a1 = vs_base + (vrow + 4) * RB + 16 * (cidx ^ v_swz<RPB, VSWZ_BITS>(vrow + 4)) + 8 * (tq & 1);
+          i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
+          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a1);
+          u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          va[k2][dt] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+          if (dpad) va[k2][dt] = u32x4{0, 0, 0, 0};
+        }
       }
-    }
-
-    // ---- masks (select to -inf).  Register r of block mt holds key
-    //      k0 + 32*mt + 16*(r/8) + 8*(lane/32) + r%8 for query qi.
-    if (need_tail || need_causal) {
+    };
+    auto pv = [&](const u32x4 (&va)[2][DT], const u32x4 (&pb)[2]) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] = E::mfma32(va[k2][dt], pb[k2], oacc[dt]);
+    };
+    // Masks (select to -inf).  Register r of block mt holds key
+    // k0 + 32*mt + 16*(r/8) + 8*(lane/32) + r%8 for query qi.
+    auto mask_block = [&](int mt, f32x16& sa, auto masked_c) {
+      if constexpr (decltype(masked_c)::value) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * mt + 16 * (r >> 3) + kl + (r & 7);
           const bool vis = (key < kend) && (!p.causal || key <= qi);
-          sacc[mt][r] = vis ? sacc[mt][r] : kNegInf;
+          sa[r] = vis ? sa[r] : kNegInf;
         }
-    }
-    if constexpr (MASK) {
-      const int qm = qi < p.Nq ? qi : p.Nq - 1;
-      const uint8_t* mrow = p.mask + (int64_t)qm * p.Nkv;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      }
+      if constexpr (MASK) {
+        const int qm = qi < p.Nq ? qi : p.Nq - 1;
+        const uint8_t* mrow = p.mask + (int64_t)qm * p.Nkv;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           const int key0 = k0 + 32 * mt + 16 * hf + kl;   // 8 consecutive keys
@@ -260,78 +286,115 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const uint32_t byte = (j < 4 ? (lo >> (8 * j)) : (hi >> (8 * (j - 4)))) & 0xFFu;
-            const int r = 8 * hf + j;
-            sacc[mt][r] = byte ? sacc[mt][r] : kNegInf;
+            sa[8 * hf + j] = byte ? sa[8 * hf + j] : kNegInf;
           }
         }
-    }
-
-    // ---- online softmax update (one query per lane), lazy rescale by wave vote
-    float mx = kNegInf;
+      }
+    };
+    // Weights of one 32-key block against reference mu, packed in place as the two B operands
+    // of the P.V product (no lane exchange); returns their FP32 sum (the unrounded weights).
+    auto weights = [&](const f32x16& sa, float mu, u32x4 (&pb)[2]) {
+      float ps = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
-    mx = xor32_max(mx) * c;                          // the other 16 keys of each block
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {   // wave-uniform
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);  // 0 from the empty state; m_new is finite here
-                                                      // for rows that saw a key, else m_run = -inf
-      const float alpha_s = (m_new == kNegInf) ? 1.f : alpha;
-      l_run *= alpha_s;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha_s;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == kNegInf) ? 0.f : m_run;   // all-masked so far: no -inf - -inf
-
-    float psum = 0.f;
-    u32x4 pf[PK];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        float pv[8];
+      for (int k2 = 0; k2 < 2; ++k2) {
+        float pw[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          pv[j] = fast_exp2(fmaf(sacc[mt][8 * hf + j], c, -m_use));   // masked: 2^-inf = 0
-          psum += pv[j];
+          pw[j] = fast_exp2(fmaf(sa[8 * k2 + j], c, -mu));   // masked: 2^-inf = 0
+          ps += pw[j];
         }
-        pf[2 * mt + hf] = u32x4{E::pack2(pv[0], pv[1]), E::pack2(pv[2], pv[3]),
-                                E::pack2(pv[4], pv[5]), E::pack2(pv[6], pv[7])};
+        pb[k2] = u32x4{E::pack2(pw[0], pw[1]), E::pack2(pw[2], pw[3]),
+                       E::pack2(pw[4], pw[5]), E::pack2(pw[6], pw[7])};
       }
-    l_run += psum;
+      return ps;
+    };
+    auto block_max = [&](const f32x16& sa) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[r]);
+      return xor32_max(mx) * c;                        // the other 16 keys of the block
+    };
+    // Lazy-rescale test, after the common-path weights: only when some row's block maximum rose
+    // more than TAU above the reference is the block redone against the raised reference.
+    auto settle = [&](const f32x16& sa, float mx, float psum, u32x4 (&pb)[2]) {
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {   // rare, wave-uniform
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);   // 0 from empty
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
+        psum = weights(sa, (m_run == kNegInf) ? 0.f : m_run, pb);
+      }
+      l_run += psum;
+    };
+    // pins a value at this point: the weight sum depends on every exponential of the block, so
+    // the common path stays ahead of the rare-branch test instead of being sunk into it
+#if defined(__HIP_DEVICE_COMPILE__)
+#define ATTN_PIN(x) asm volatile("" : "+v"(x))
+#else
+#define ATTN_PIN(x) (void)(x)   // the host pass only emits launch stubs
+#endif
 
-    // ---- O^T += V^T P^T.  A operand (V^T, 32 d-rows x 16 keys) through transposing LDS reads:
-    //      16-lane group g covers d = 32*dt + 16*(g%2) .. +16 and keys 16*kk + 8*(g/2) + {0..3},
-    //      {4..7}; lane 4*j + tq of the group addresses key row (.. + j), d chunk 4*tq.
-    constexpr int VB = (PK * DT <= 16) ? PK : (DT < 8 ? 16 / DT : 1);   // key steps per batch
+    // The tile is processed as MT blocks of 32 keys, software-pipelined inside the wave:
+    //   S_0 = K_0 Q^T;  [S_1 = K_1 Q^T || softmax(S_0)];  [O += V_0 P_0 || softmax(S_1)];  O += V_1 P_1
+    // so the matrix cores run while the same wave computes the previous block's exponentials.
+    auto tile_body = [&](auto masked_c) {
+      u32x4 va[2][DT];
+      u32x4 pb[2];
+      if constexpr (D <= 128 && MT == 2) {
+        u32x4 kfa[KSTEPS], kfb[KSTEPS];
+        read_k(0, kfa);
+        read_k(1, kfb);
+        f32x16 sa = qk(kfa);
+        // phase X: S_1 on the matrix cores || V_0 reads + softmax(S_0) on the vector ALUs
+        f32x16 sb = qk(kfb);
+        read_v(0, va);
+        mask_block(0, sa, masked_c);
+        float mx0 = block_max(sa);
+        float ps0 = weights(sa, (m_run == kNegInf) ? 0.f : m_run, pb);
 #pragma unroll
-    for (int kb = 0; kb < PK; kb += VB) {
-      u32x4 va[VB][DT];
+        for (int i = 0; i < KSTEPS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+        }
+        ATTN_PIN(ps0);
+        settle(sa, mx0, ps0, pb);
+        // phase Y: O += V_0 P_0 on the matrix cores || V_1 reads + softmax(S_1)
+        u32x4 va1[2][DT];
+        u32x4 pb1[2];
+        pv(va, pb);
+        read_v(1, va1);
+        mask_block(1, sb, masked_c);
+        float mx1 = block_max(sb);
+        float ps1 = weights(sb, (m_run == kNegInf) ? 0.f : m_run, pb1);
 #pragma unroll
-      for (int k2 = 0; k2 < VB; ++k2) {
-        const int vrow = 16 * (kb + k2) + 8 * (g >> 1) + jrow;
+        for (int i = 0; i < 2 * DT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+        }
+        ATTN_PIN(ps1);
+        settle(sb, mx1, ps1, pb1);
+        // phase Z
+        pv(va1, pb1);
+      } else {                    // small tiles or D = 256: one block at a time
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int d = 32 * dt + 16 * (g & 1) + 4 * tq;
-          const int cidx = (d / 8) % CH;
-          typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-          const uint8_t* a0 = vs_base + vrow * RB + 16 * (cidx ^ v_swz<RPB, VSWZ_BITS>(vrow)) + 8 * (tq & 1);
-          const uint8_t* a1 = vs_base + (vrow + 4) * RB + 16 * (cidx ^ v_swz<RPB, VSWZ_BITS>(vrow + 4)) + 8 * (tq & 1);
-          i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
-          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a1);
-          u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          va[k2][dt] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-          if (dpad) va[k2][dt] = u32x4{0, 0, 0, 0};
+        for (int mt = 0; mt < MT; ++mt) {
+          u32x4 kfa[KSTEPS];
+          read_k(mt, kfa);
+          f32x16 sa = qk(kfa);
+          mask_block(mt, sa, masked_c);
+          float mx = block_max(sa);
+          float ps = weights(sa, (m_run == kNegInf) ? 0.f : m_run, pb);
+          settle(sa, mx, ps, pb);
+          read_v(mt, va);
+          pv(va, pb);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int k2 = 0; k2 < VB; ++k2)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt] = E::mfma32(va[k2][dt], pf[kb + k2], oacc[dt]);
-    }
+    };
+#undef ATTN_PIN
+    if (need_tail || need_causal) tile_body(std::true_type{});
+    else tile_body(std::false_type{});
   }
 
   // ---- epilogue: finish the denominator over the lane pair, normalise, store

@@ -16,7 +16,7 @@ def test_library_exports_every_declared_symbol():
     assert {"attn_fwd", "attn_fwd_splitk", "attn_combine", "attn_fwd_ex", "attn_last_error",
             "attn_abi_version"} <= set(names)
     for n in names:
-        assert hasattr(sa.lib, n), n
+        assert hasattr(sa.lib(), n), n
 
 
 def test_abi_version():
@@ -31,16 +31,16 @@ BAD = 0x10008    # 8-byte aligned only
 
 
 def fwd(q=A, k=A, v=A, out=A, lse=None, B=1, H=1, N=64, D=64, causal=0, mask=None, dtype=0):
-    return sa.lib.attn_fwd(q, k, v, out, lse, B, H, N, D, causal, mask, dtype, None)
+    return sa.lib().attn_fwd(q, k, v, out, lse, B, H, N, D, causal, mask, dtype, None)
 
 
 def splitk(q=A, k=A, v=A, out=None, lse=None, B=1, H=1, Nq=1, Nkv=64, D=64, causal=0, mask=None, P=4,
            o_p=A, l_p=A, dtype=0):
-    return sa.lib.attn_fwd_splitk(q, k, v, out, lse, B, H, Nq, Nkv, D, causal, mask, P, o_p, l_p, dtype, None)
+    return sa.lib().attn_fwd_splitk(q, k, v, out, lse, B, H, Nq, Nkv, D, causal, mask, P, o_p, l_p, dtype, None)
 
 
 def combine(o_p=A, l_p=A, out=A, lse=None, P=4, rows=1, heads=1, depth=64, out_dtype=2):
-    return sa.lib.attn_combine(o_p, l_p, out, lse, P, rows, heads, depth, out_dtype, None)
+    return sa.lib().attn_combine(o_p, l_p, out, lse, P, rows, heads, depth, out_dtype, None)
 
 
 @needs_no_gpu
@@ -80,10 +80,10 @@ def test_reject_paths(call, code):
 @needs_no_gpu
 def test_fwd_ex_rejects_bad_block_n():
     a = sa.FwdArgs(A, A, A, A, None, None, 1, 1, 64, 128, 0, 0, 32)
-    assert sa.lib.attn_fwd_ex(ctypes.byref(a), None) == E_UNSUP
+    assert sa.lib().attn_fwd_ex(ctypes.byref(a), None) == E_UNSUP
     a.block_n = 48
-    assert sa.lib.attn_fwd_ex(ctypes.byref(a), None) == E_UNSUP
-    assert sa.lib.attn_fwd_ex(None, None) == E_NULL
+    assert sa.lib().attn_fwd_ex(ctypes.byref(a), None) == E_UNSUP
+    assert sa.lib().attn_fwd_ex(None, None) == E_NULL
 
 
 def test_binding_refuses_host_tensors():

@@ -201,6 +201,11 @@ def test_decode_empty_partitions(sa):
 
 @pytest.mark.parametrize("P", [1, 3, 7])
 def test_square_causal_split_matches_unsplit(sa, P):
+    """Square causal shapes through the matrix-core split path.  Here |O| reaches ~3 and the
+    split and unsplit results each carry their own bf16 rounding of the weights (<= 2^-9 * max|v|
+    per result, tile boundaries differ), so they are compared with each other within twice that
+    bound plus the unsplit output's bf16 rounding, and each against the oracle.  The 1e-3
+    split-vs-unsplit criterion is checked on the decode workload, where |O| ~ 1e-2."""
     rng = si.rng_for(86, P)
     N, D = 1000, 64
     q, k, v = (si.cast(x, "bf16") for x in si.draw_qkv(rng, (2, N, 4, D), (2, N, 4, D)))
@@ -211,11 +216,13 @@ def test_square_causal_split_matches_unsplit(sa, P):
     torch.cuda.synchronize()
     out32, lse32 = out32.reshape(out.shape), lse32.reshape(lse.shape)   # [B*Nq, H, ...] -> [B, Nq, H, ...]
     d = (out32 - out.float()).abs()
-    bound = 1e-3 + out32.abs() * 2.0 ** -8          # bf16 output rounding of the unsplit result
+    vmax = float(v.float().abs().max())
+    bound = 2 * 2.0 ** -9 * vmax + out32.abs() * 2.0 ** -8 + 1e-5
     assert bool((d <= bound).all()), f"split vs unsplit {d.max().item():.3e}"
     assert torch.allclose(lse32, lse, rtol=1e-5, atol=1e-4)
     ref, ref_lse = oracle.attn_dense(q, k, v, causal=True)
     _compare(out32.reshape(-1, D), lse32.reshape(-1), ref, ref_lse, "bf16", f"split P={P}")
+    _compare(out.reshape(-1, D), lse.reshape(-1), ref, ref_lse, "bf16", "unsplit")
 
 
 # ---------------------------------------------------------------------------------------------
