@@ -10,9 +10,10 @@
 // log2 units (logit * log2(e)), so every exponential is one v_exp_f32.
 //
 // Work decomposition (CDNA4 form of the pages' ownership rule that a row reduction must stay
-// inside one wave): one workgroup of four waves per (query block of 128 rows, head, batch,
+// inside one wave): one workgroup of WAVES waves per (query block of 32*WAVES rows, head, batch,
 // partition); each wave owns 32 whole query rows and the block's full key range, so no
-// cross-wave exchange is ever needed.
+// cross-wave exchange is ever needed.  The waves share the K and V tiles, which are staged
+// into LDS by direct global-to-LDS loads, two stages deep, one barrier per tile.
 //
 // Transposed products: the kernel computes S^T = K Q^T and O^T = V^T P^T.  In both
 // accumulators a lane owns one query COLUMN, so the per-query state (m, l, alpha) is one scalar
@@ -33,9 +34,8 @@
 
 namespace attn {
 
-constexpr int kWaves = 4;
-constexpr int kRowsPerWave = 32;
-constexpr int kBlockM = kWaves * kRowsPerWave;  // 128 query rows per workgroup
+constexpr int kRowsPerWave = 32;               // query rows (accumulator columns) per wave
+constexpr int kMinBlockM = 4 * kRowsPerWave;   // smallest query block (four waves)
 
 // Row permutation of a 32-key block inside the first product: A-operand row i holds key pi(i).
 // With it, accumulator register r of lane l holds key 16*(r/8) + 8*(l/32) + (r%8), which is
@@ -45,10 +45,12 @@ __device__ __forceinline__ int key_perm(int i) {
   return ((b >> 1) << 4) + (h << 3) + ((b & 1) << 2) + (i & 3);
 }
 
-// Lazy rescale threshold (log2 units): the reference maximum m is raised only when some row of
-// the wave sees a score more than TAU above it, so weights stay <= 2^TAU and the O rescale is
-// skipped on most tiles.  O / l and m + log2(l) do not depend on which reference is used.
+// Lazy rescale threshold (log2 units): the reference maximum m is raised only when a weight
+// against the current reference could exceed 2^TAU, so weights stay <= 2^TAU and the O rescale
+// is skipped on almost every block.  O / l and m + log2(l) do not depend on which reference is
+// used.
 constexpr float kTau = 8.0f;
+constexpr float kTauPow = 256.0f;   // 2^TAU
 
 // LDS chunk swizzles (16-byte chunk index XOR, per key row).
 template <int SWZ>
@@ -56,9 +58,13 @@ __device__ __forceinline__ int k_swz(int row) { return row & SWZ; }
 template <int RPB, int BITS>
 __device__ __forceinline__ int v_swz(int row) { return BITS ? 4 * ((row / RPB) & BITS) : 0; }
 
-template <typename T, int D, int BN, bool MASK, bool SPLIT>
-__global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdParams p) {
+template <int S> using stage_t = std::integral_constant<int, S>;
+
+// WAVES waves of 32 query rows each; BN keys per tile.
+template <typename T, int D, int BN, bool MASK, bool SPLIT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void attn_fwd_kernel(FwdParams p) {
   using E = elem<T>;
+  constexpr int kBlockM = WAVES * kRowsPerWave;
   constexpr int DP = D < 32 ? 32 : D;   // rows of O^T (padded to one 32-row MFMA tile)
   constexpr int RB = D * 2;             // bytes per K / V row in LDS (unpadded)
   constexpr int CH = D / 8;             // 16-byte chunks per row
@@ -72,10 +78,15 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
   constexpr int KSTEPS = D / 16;        // k-steps of S^T = K Q^T
   constexpr int MT = BN / 32;           // 32-key blocks per tile
   constexpr int DT = DP / 32;           // 32-row tiles of O^T
+  static_assert(WAVES == 4 || WAVES == 8, "four or eight waves per workgroup");
   static_assert(TILE % 1024 == 0, "tile must be a whole number of 1 KiB wave loads");
+  // LDS: [K stage 0 | K stage 1 | V stage 0 | V stage 1].  Every operand read is a per-lane base
+  // plus a compile-time offset (block, key step, stage), which must fit the 16-bit DS offset.
+  constexpr int K_OFS = 0, V_OFS = 2 * TILE;
+  static_assert(TILE + (MT - 1) * 32 * RB < 65536, "K read offsets exceed the DS immediate");
+  static_assert(TILE + (BN - 1) * RB < 65536, "V read offsets exceed the DS immediate");
 
-  // two stages of (K, V)
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * 2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -84,12 +95,25 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
   // ---- block coordinates.  Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8),
   //      so the linear order is remapped to give each XCD a contiguous run of blocks: the query
   //      blocks of one (head, batch) then run together on one XCD and share its L2 for K and V.
+  //      Causal blocks differ in length (query block i visits i+1 key blocks), so they are issued
+  //      longest first, and over PAIRS of heads: with one head at a time the long blocks of the
+  //      last heads would start late and finish after everything else.
   int bid = blockIdx.x;
   if (gridDim.x % 8 == 0) bid = (bid % 8) * (gridDim.x / 8) + bid / 8;
-  const int qb_idx = bid % p.n_qblocks; bid /= p.n_qblocks;
-  const int h = bid % p.H; bid /= p.H;
-  const int b = bid % p.B; bid /= p.B;
-  const int part = bid;
+  const int n_heads = p.H * p.B * p.P;                 // (head, batch, partition) units
+  int hl, qb_idx;
+  if (p.causal && n_heads % 2 == 0) {
+    const int hh = bid & 1;
+    bid >>= 1;
+    qb_idx = bid % p.n_qblocks;
+    hl = 2 * (bid / p.n_qblocks) + hh;
+  } else {
+    qb_idx = bid % p.n_qblocks;
+    hl = bid / p.n_qblocks;
+  }
+  const int h = hl % p.H;
+  const int b = (hl / p.H) % p.B;
+  const int part = hl / (p.H * p.B);
   const int qb = p.causal ? (p.n_qblocks - 1 - qb_idx) : qb_idx;   // causal: longest first
 
   const int q_block0 = qb * kBlockM;
@@ -113,30 +137,32 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
   //      LDS bytes [1024 j, 1024 j + 1024): lane l lands at row j*RPI + l/CH, physical chunk
   //      l%CH, which holds logical chunk (l%CH) ^ swizzle(row) of that key row.  The per-lane
   //      byte offsets inside a tile are fixed; each tile only moves the scalar base.
-  constexpr int PER_WAVE = (NT + kWaves - 1) / kWaves;
-  // Row of instruction jj = (jj*4 + wave)*RPI + lane/CH.  When 4*RPI is a multiple of 16 (D <= 128)
-  // neither swizzle depends on jj, so one per-lane offset serves every instruction and the jj
-  // part goes into the scalar offset.
-  constexpr bool ONE_OFS = (4 * RPI) % 16 == 0;
+  constexpr int PER_WAVE = (NT + WAVES - 1) / WAVES;
+  // Row of instruction jj = (jj*WAVES + wave)*RPI + lane/CH.  When WAVES*RPI is a multiple of 16
+  // (D <= 128) neither swizzle depends on jj, so one per-lane offset serves every instruction and
+  // the jj part goes into the scalar offset.
+  constexpr bool ONE_OFS = (WAVES * RPI) % 16 == 0;
   const int ld_row_in = lane / CH;
   const int ld_pc = lane % CH;
   const int row0 = wave * RPI + ld_row_in;
   const uint32_t kvo0 = (uint32_t)(((int64_t)row0 * row_stride + 8 * (ld_pc ^ k_swz<SWZ>(row0))) * 2);
   const uint32_t vvo0 = (uint32_t)(((int64_t)row0 * row_stride + 8 * (ld_pc ^ v_swz<RPB, VSWZ_BITS>(row0))) * 2);
-  const uint32_t jj_bytes = (uint32_t)((int64_t)kWaves * RPI * row_stride * 2);   // scalar step per jj
+  const uint32_t jj_bytes = (uint32_t)((int64_t)WAVES * RPI * row_stride * 2);   // scalar step per jj
   const uint32_t tile_bytes = (uint32_t)((int64_t)BN * row_stride * 2);
-  auto issue_tile = [&](int t, int stage) {
+  // the LDS destination goes to M0, which must be provably wave-uniform
+  const int wave_lds = __builtin_amdgcn_readfirstlane(wave * 1024);
+  auto issue_tile = [&](int t, auto stage_c) {
+    constexpr int S = decltype(stage_c)::value;
     const int k0 = kbeg + t * BN;
-    // the LDS destination goes to M0, which must be provably wave-uniform
-    uint8_t* kdst = lds + __builtin_amdgcn_readfirstlane(stage * 2 * TILE + wave * 1024);
-    uint8_t* vdst = kdst + TILE;
+    uint8_t* kdst = lds + K_OFS + S * TILE + wave_lds;
+    uint8_t* vdst = lds + V_OFS + S * TILE + wave_lds;
     __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)k0 * row_stride), 0, tile_bytes, 0x00020000);
     __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)k0 * row_stride), 0, tile_bytes, 0x00020000);
     if (k0 + BN <= p.Nkv) {
 #pragma unroll
       for (int jj = 0; jj < PER_WAVE; ++jj) {
-        const int j = jj * kWaves + wave;
-        if (NT % kWaves != 0 && j >= NT) break;
+        const int j = jj * WAVES + wave;
+        if (NT % WAVES != 0 && j >= NT) break;
         uint32_t ko = kvo0, vo = vvo0, so = jj * jj_bytes;
         if constexpr (!ONE_OFS) {   // the swizzles depend on the instruction: per-lane offsets
           const int row = j * RPI + ld_row_in;
@@ -144,20 +170,20 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
           vo = (uint32_t)(((int64_t)row * row_stride + 8 * (ld_pc ^ v_swz<RPB, VSWZ_BITS>(row))) * 2);
           so = 0;
         }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kdst + jj * kWaves * 1024), 16, ko, so, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + jj * kWaves * 1024), 16, vo, so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kdst + jj * WAVES * 1024), 16, ko, so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + jj * WAVES * 1024), 16, vo, so, 0, 0);
       }
     } else {   // last tile: rows past the end are masked; read the last valid row instead
 #pragma unroll
       for (int jj = 0; jj < PER_WAVE; ++jj) {
-        const int j = jj * kWaves + wave;
-        if (NT % kWaves != 0 && j >= NT) break;
+        const int j = jj * WAVES + wave;
+        if (NT % WAVES != 0 && j >= NT) break;
         const int row = j * RPI + ld_row_in;
         const int rr = (k0 + row < p.Nkv ? k0 + row : p.Nkv - 1) - k0;
         const uint32_t ko = (uint32_t)(((int64_t)rr * row_stride + 8 * (ld_pc ^ k_swz<SWZ>(row))) * 2);
         const uint32_t vo = (uint32_t)(((int64_t)rr * row_stride + 8 * (ld_pc ^ v_swz<RPB, VSWZ_BITS>(row))) * 2);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kdst + jj * kWaves * 1024), 16, ko, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + jj * kWaves * 1024), 16, vo, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kdst + jj * WAVES * 1024), 16, ko, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + jj * WAVES * 1024), 16, vo, 0, 0, 0);
       }
     }
   };
@@ -185,40 +211,63 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
   const bool wave_has_rows = q0 < p.Nq;
   const int kl = 8 * (lane >> 5);
 
-  // per-lane LDS byte offsets of the operand reads (stage-relative)
-  int koff[MT];
+  // ---- per-lane LDS byte addresses of the operand reads.  K operand (block mt, key step ks):
+  //      row mt*32 + pi(lane%32), logical chunk 2*ks + lane/32, XOR the row swizzle (equal for
+  //      every block since SWZ < 32).  V^T operand (block mt, key step k2, row tile dt) by
+  //      transposing reads: 16-lane group g covers d = 32*dt + 16*(g%2) .. +16 and keys
+  //      16*(2*mt + k2) + 8*(g/2) + {0..3}, {4..7}; lane 4*j + tq of the group addresses key row
+  //      (.. + j), d chunk 4*tq.  Only the parts that depend on the lane are kept here; block,
+  //      key step and stage are compile-time offsets.
+  const uint8_t* kaddr[KSTEPS];
+  {
+    const int krow = key_perm(lane & 31);
+    const int ksw = k_swz<SWZ>(krow);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) koff[mt] = (mt * 32 + key_perm(lane & 31)) * RB;
-  const int krow_swz = k_swz<SWZ>(key_perm(lane & 31));   // equal for mt*32 + r: SWZ < 32
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      kaddr[ks] = lds + K_OFS + krow * RB + 16 * ((2 * ks + (lane >> 5)) ^ ksw);
+  }
+  const uint8_t* vaddr[DT];
   const int g = lane >> 4, li = lane & 15;
-  const int jrow = li >> 2, tq = li & 3;
   const bool dpad = (D < 32) && ((g & 1) != 0);    // O^T rows D..31 for D = 16: zero operand
+  {
+    const int jrow = li >> 2, tq = li & 3;
+    const int vrow = 8 * (g >> 1) + jrow;          // the swizzle depends on the key row only through this
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = 32 * dt + 16 * (g & 1) + 4 * tq;
+      const int cidx = (d / 8) % CH;
+      vaddr[dt] = lds + V_OFS + vrow * RB + 16 * (cidx ^ v_swz<RPB, VSWZ_BITS>(vrow)) + 8 * (tq & 1);
+    }
+  }
 
-  if (ntiles > 0) issue_tile(0, 0);
+  // pins a value at this point: the weight sum depends on every exponential of the block, so
+  // the common path stays ahead of the rare-branch test instead of being sunk into it
+#if defined(__HIP_DEVICE_COMPILE__)
+#define ATTN_PIN(x) asm volatile("" : "+v"(x))
+#else
+#define ATTN_PIN(x) (void)(x)   // the host pass only emits launch stubs
+#endif
 
-  for (int t = 0; t < ntiles; ++t) {
+  // ---- one key tile: wait for it, start the next tile's loads, update the state
+  auto do_tile = [&](const int t, auto stage_c) {
+    constexpr int S = decltype(stage_c)::value;
     const int k0 = kbeg + t * BN;
-    const int stage = t & 1;
     // tile t resident for every wave (its LDS-DMA loads are counted by vmcnt, which the
     // barrier's own fence does not wait for); every wave done with tile t-1's stage
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < ntiles) issue_tile(t + 1, stage ^ 1);
+    if (t + 1 < ntiles) issue_tile(t + 1, stage_t<S ^ 1>{});
 
     // wave-uniform decisions for this tile
     const bool future = p.causal && (k0 > q0 + kRowsPerWave - 1);   // no key visible to any row
-    if (!wave_has_rows || future) continue;
+    if (!wave_has_rows || future) return;
     const bool need_tail = (k0 + BN > kend);
     const bool need_causal = p.causal && (k0 + BN - 1 > q0);
-    const uint8_t* ks_base = lds + stage * 2 * TILE;
-    const uint8_t* vs_base = ks_base + TILE;
 
     auto read_k = [&](int mt, u32x4 (&kf)[KSTEPS]) {
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int cidx = (2 * ks + (lane >> 5)) ^ krow_swz;
-        kf[ks] = *reinterpret_cast<const u32x4*>(ks_base + koff[mt] + 16 * cidx);
-      }
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        kf[ks] = *reinterpret_cast<const u32x4*>(kaddr[ks] + S * TILE + mt * 32 * RB);
     };
     auto qk = [&](const u32x4 (&kf)[KSTEPS]) {
       f32x16 acc = f32x16{};
@@ -226,27 +275,19 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
       for (int ks = 0; ks < KSTEPS; ++ks) acc = E::mfma32(kf[ks], qf[ks], acc);
       return acc;
     };
-    // V^T fragments of the two 16-key steps of block mt: 16-lane group g covers
-    // d = 32*dt + 16*(g%2) .. +16 and keys 16*kk + 8*(g/2) + {0..3}, {4..7}; lane 4*j + tq of the
-    // group addresses key row (.. + j), d chunk 4*tq.
     auto read_v = [&](int mt, u32x4 (&va)[2][DT]) {
+      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const int vrow = 16 * (2 * mt + k2) + 8 * (g >> 1) + jrow;
+      for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int d = 32 * dt + 16 * (g & 1) + 4 * tq;
-          const int cidx = (d / 8) % CH;
-          typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-          const uint8_t* a0 = vs_base + vrow * RB + 16 * (cidx ^ v_swz<RPB, VSWZ_BITS>(vrow)) + 8 * (tq & 1);
-          const uint8_t* a1 = vs_base + (vrow + 4) * RB + 16 * (cidx ^ v_swz<RPB, VSWZ_BITS>(vrow + 4)) + 8 * (tq & 1);
+          const uint8_t* a0 = vaddr[dt] + S * TILE + 16 * (2 * mt + k2) * RB;
           i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
-          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a1);
+          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 4 * RB));
           u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
           va[k2][dt] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
           if (dpad) va[k2][dt] = u32x4{0, 0, 0, 0};
         }
-      }
     };
     auto pv = [&](const u32x4 (&va)[2][DT], const u32x4 (&pb)[2]) {
 #pragma unroll
@@ -314,87 +355,109 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[r]);
       return xor32_max(mx) * c;                        // the other 16 keys of the block
     };
-    // Lazy-rescale test, after the common-path weights: only when some row's block maximum rose
-    // more than TAU above the reference is the block redone against the raised reference.
-    auto settle = [&](const f32x16& sa, float mx, float psum, u32x4 (&pb)[2]) {
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {   // rare, wave-uniform
-        const float m_new = fmaxf(m_run, mx);
+    // Softmax of one block, in two parts: start() masks and computes the weights against the
+    // current reference; finish() is the lazy-rescale test, which the caller places after the
+    // weights.  Only when some weight of the wave could exceed 2^TAU is the reference raised to
+    // the block maximum, the state rescaled and the block redone (rare, wave-uniform):
+    //   exact test (tiles with masked keys): block maximum > m + TAU;
+    //   sum test (every key visible): the lane's weight sum > 2^TAU, or no reference yet.  Every
+    //   weight is at most the sum, so a pass keeps every weight <= 2^TAU; and once a visible key
+    //   has set the reference (so l >= 1), weights that underflow to 0 are negligible.
+    struct BlockSm { float mx, ps; };
+    auto sm_start = [&](int mt, f32x16& sa, u32x4 (&pb)[2], auto masked_c) {
+      constexpr bool exact = decltype(masked_c)::value || MASK;
+      mask_block(mt, sa, masked_c);
+      BlockSm st{kNegInf, 0.f};
+      if constexpr (exact) st.mx = block_max(sa);
+      st.ps = weights(sa, (m_run == kNegInf) ? 0.f : m_run, pb);
+      return st;
+    };
+    auto sm_finish = [&](BlockSm st, const f32x16& sa, u32x4 (&pb)[2], auto masked_c) {
+      constexpr bool exact = decltype(masked_c)::value || MASK;
+      ATTN_PIN(st.ps);
+      bool raise;
+      if constexpr (exact) raise = __builtin_amdgcn_ballot_w64(st.mx > m_run + kTau) != 0;
+      else raise = __builtin_amdgcn_ballot_w64(st.ps > kTauPow || m_run == kNegInf) != 0;
+      if (raise) {
+        if constexpr (!exact) st.mx = block_max(sa);
+        const float m_new = fmaxf(m_run, st.mx);
         const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);   // 0 from empty
         l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
         m_run = m_new;
-        psum = weights(sa, (m_run == kNegInf) ? 0.f : m_run, pb);
+        st.ps = weights(sa, (m_run == kNegInf) ? 0.f : m_run, pb);
       }
-      l_run += psum;
+      l_run += st.ps;
     };
-    // pins a value at this point: the weight sum depends on every exponential of the block, so
-    // the common path stays ahead of the rare-branch test instead of being sunk into it
-#if defined(__HIP_DEVICE_COMPILE__)
-#define ATTN_PIN(x) asm volatile("" : "+v"(x))
-#else
-#define ATTN_PIN(x) (void)(x)   // the host pass only emits launch stubs
-#endif
 
-    // The tile is processed as MT blocks of 32 keys, software-pipelined inside the wave:
-    //   S_0 = K_0 Q^T;  [S_1 = K_1 Q^T || softmax(S_0)];  [O += V_0 P_0 || softmax(S_1)];  O += V_1 P_1
-    // so the matrix cores run while the same wave computes the previous block's exponentials.
     auto tile_body = [&](auto masked_c) {
       u32x4 va[2][DT];
       u32x4 pb[2];
-      if constexpr (D <= 128 && MT == 2) {
-        u32x4 kfa[KSTEPS], kfb[KSTEPS];
-        read_k(0, kfa);
-        read_k(1, kfb);
-        f32x16 sa = qk(kfa);
-        // phase X: S_1 on the matrix cores || V_0 reads + softmax(S_0) on the vector ALUs
-        f32x16 sb = qk(kfb);
-        read_v(0, va);
-        mask_block(0, sa, masked_c);
-        float mx0 = block_max(sa);
-        float ps0 = weights(sa, (m_run == kNegInf) ? 0.f : m_run, pb);
+      if constexpr (D <= 128 && MT >= 2) {
+        // Software pipeline over the MT blocks of the tile: phase k issues the matrix work
+        // S_{k+1} = K_{k+1} Q^T and O += V_{k-1} P_{k-1} and, on the vector ALUs meanwhile,
+        // softmax(S_k), which depends on neither:
+        //   S_0;  [S_1 || sm(S_0)];  [S_2, O += V_0 P_0 || sm(S_1)];  ...;  O += V_{MT-1} P_{MT-1}
+        u32x4 kf[KSTEPS];
+        u32x4 pb_prev[2];
+        read_k(0, kf);
+        f32x16 s_cur = qk(kf);
+        // S_0 completes on its own: otherwise the scheduler interleaves S_1 with it and leaves
+        // no matrix work to overlap softmax(S_0)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < KSTEPS; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
-        }
-        ATTN_PIN(ps0);
-        settle(sa, mx0, ps0, pb);
-        // phase Y: O += V_0 P_0 on the matrix cores || V_1 reads + softmax(S_1)
-        u32x4 va1[2][DT];
-        u32x4 pb1[2];
-        pv(va, pb);
-        read_v(1, va1);
-        mask_block(1, sb, masked_c);
-        float mx1 = block_max(sb);
-        float ps1 = weights(sb, (m_run == kNegInf) ? 0.f : m_run, pb1);
+        for (int k = 0; k <= MT; ++k) {
+          f32x16 s_nxt = f32x16{};
+          if (k + 1 < MT) read_k(k + 1, kf);
+          if (k >= 1) read_v(k - 1, va);
+          if (k + 1 < MT) s_nxt = qk(kf);
+          if (k >= 1) pv(va, pb_prev);
+          if (k < MT) {
+            BlockSm st = sm_start(k, s_cur, pb, masked_c);
+            const int n_mfma = (k + 1 < MT ? KSTEPS : 0) + (k >= 1 ? 2 * DT : 0);
+            if (n_mfma > KSTEPS) {
 #pragma unroll
-        for (int i = 0; i < 2 * DT; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+              for (int i = 0; i < n_mfma; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
+              }
+            } else {
+#pragma unroll
+              for (int i = 0; i < n_mfma; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+              }
+            }
+            sm_finish(st, s_cur, pb, masked_c);
+            pb_prev[0] = pb[0];
+            pb_prev[1] = pb[1];
+            s_cur = s_nxt;
+          }
         }
-        ATTN_PIN(ps1);
-        settle(sb, mx1, ps1, pb1);
-        // phase Z
-        pv(va1, pb1);
-      } else {                    // small tiles or D = 256: one block at a time
+      } else {                    // one block at a time (BN = 32, D = 256)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           u32x4 kfa[KSTEPS];
           read_k(mt, kfa);
           f32x16 sa = qk(kfa);
-          mask_block(mt, sa, masked_c);
-          float mx = block_max(sa);
-          float ps = weights(sa, (m_run == kNegInf) ? 0.f : m_run, pb);
-          settle(sa, mx, ps, pb);
+          BlockSm st = sm_start(mt, sa, pb, masked_c);
+          sm_finish(st, sa, pb, masked_c);
           read_v(mt, va);
           pv(va, pb);
         }
       }
     };
-#undef ATTN_PIN
     if (need_tail || need_causal) tile_body(std::true_type{});
     else tile_body(std::false_type{});
+  };
+#undef ATTN_PIN
+
+  if (ntiles > 0) issue_tile(0, stage_t<0>{});
+  // two tiles per iteration, so that the LDS stage of every operand read is a constant
+  for (int t = 0; t < ntiles; t += 2) {
+    do_tile(t, stage_t<0>{});
+    if (t + 1 < ntiles) do_tile(t + 1, stage_t<1>{});
   }
 
   // ---- epilogue: finish the denominator over the lane pair, normalise, store
@@ -441,18 +504,28 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void attn_fwd_kernel(FwdPa
 }
 
 // ---- host-side dispatch -------------------------------------------------------------------
-template <typename T, int D, int BN, bool MASK, bool SPLIT>
-static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
+#ifndef FWD_WAVES
+#define FWD_WAVES(D) 4
+#endif
+#ifndef FWD_BN128
+#define FWD_BN128 64
+#endif
+
+template <typename T, int D, int BN, bool MASK, bool SPLIT, int WAVES>
+static hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t s) {
+  FwdParams p = p0;
+  p.n_qblocks = (p.Nq + WAVES * kRowsPerWave - 1) / (WAVES * kRowsPerWave);
   dim3 grid((unsigned)((int64_t)p.n_qblocks * p.H * p.B * p.P));
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, MASK, SPLIT>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, MASK, SPLIT, WAVES>), grid, dim3(64 * WAVES), 0, s, p);
   return hipGetLastError();
 }
 
 template <typename T, int D, int BN>
 static hipError_t launch_fwd_mask(const FwdParams& p, bool split, hipStream_t s) {
+  constexpr int W = FWD_WAVES(D);
   const bool mask = p.mask != nullptr;
-  if (split) return mask ? launch_fwd_t<T, D, BN, true, true>(p, s) : launch_fwd_t<T, D, BN, false, true>(p, s);
-  return mask ? launch_fwd_t<T, D, BN, true, false>(p, s) : launch_fwd_t<T, D, BN, false, false>(p, s);
+  if (split) return mask ? launch_fwd_t<T, D, BN, true, true, W>(p, s) : launch_fwd_t<T, D, BN, false, true, W>(p, s);
+  return mask ? launch_fwd_t<T, D, BN, true, false, W>(p, s) : launch_fwd_t<T, D, BN, false, false, W>(p, s);
 }
 
 template <typename T>
@@ -461,7 +534,7 @@ static hipError_t launch_fwd_dtype(const FwdParams& p, int D, int BN, bool split
     case 16: return BN == 32 ? launch_fwd_mask<T, 16, 32>(p, split, s) : launch_fwd_mask<T, 16, 64>(p, split, s);
     case 32: return BN == 32 ? launch_fwd_mask<T, 32, 32>(p, split, s) : launch_fwd_mask<T, 32, 64>(p, split, s);
     case 64: return BN == 32 ? launch_fwd_mask<T, 64, 32>(p, split, s) : launch_fwd_mask<T, 64, 64>(p, split, s);
-    case 128: return launch_fwd_mask<T, 128, 64>(p, split, s);
+    case 128: return launch_fwd_mask<T, 128, FWD_BN128>(p, split, s);
     case 256: return launch_fwd_mask<T, 256, 64>(p, split, s);
   }
   return hipErrorInvalidValue;
@@ -471,6 +544,6 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int BN, bool split, 
   return dtype == 0 ? launch_fwd_dtype<bf16_t>(p, D, BN, split, s) : launch_fwd_dtype<f16_t>(p, D, BN, split, s);
 }
 
-int fwd_block_m() { return kBlockM; }
+int fwd_block_m() { return kMinBlockM; }
 
 }  // namespace attn

@@ -21,7 +21,7 @@ struct FwdParams {
   int causal;
   int P;                // 1 when unsplit
   int chunk;            // keys per partition (split)
-  int n_qblocks;        // ceil(Nq / 128)
+  int n_qblocks;        // ceil(Nq / query rows per workgroup); set by the launcher
   int mask_vec;         // mask rows may be read 8 bytes at a time
   float scale_log2;     // log2(e) / sqrt(D)
 };

@@ -103,6 +103,39 @@ def test_single_key_is_exact(sa):
 
 
 # ---------------------------------------------------------------------------------------------
+# D = 128 (the two-group kernel): ragged lengths, several heads, both dtypes, split path
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("N", [1, 63, 333, 600])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d128_ragged(sa, N, dtype, causal):
+    rng = si.rng_for(79, N)
+    q, k, v = (si.cast(x, dtype) for x in si.draw_qkv(rng, (2, N, 3, 128), (2, N, 3, 128)))
+    out, lse = sa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+    ref, ref_lse = oracle.attn_dense(q, k, v, causal=causal)
+    _compare(out.reshape(-1, 128), lse.reshape(-1), ref, ref_lse, dtype, f"D128 N={N} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("P", [2, 5])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d128_split(sa, P, causal):
+    rng = si.rng_for(78, P)
+    N = 517
+    q, k, v = (si.cast(x, "bf16") for x in si.draw_qkv(rng, (1, N, 2, 128), (1, N, 2, 128)))
+    o_p, l_p, out, lse = sa.splitk(q.to(DEV), k.to(DEV), v.to(DEV), P, causal=causal)
+    torch.cuda.synchronize()
+    ref_op, ref_lp = oracle.splitk(q, k, v, P, causal=causal)
+    for pp in range(P):
+        _compare(o_p[pp].reshape(-1, 128), None, ref_op[pp], ref_lp[pp], "bf16", f"o_partial p={pp}")
+        lp = l_p[pp].reshape(-1).cpu().numpy().astype(np.float64)
+        fin = np.isfinite(ref_lp[pp])
+        assert np.all(lp[~fin] == -np.inf)
+        np.testing.assert_allclose(lp[fin], ref_lp[pp][fin], rtol=1e-4, atol=1e-4)
+    ref, ref_lse = oracle.attn_dense(q, k, v, causal=causal)
+    _compare(out.reshape(-1, 128), lse.reshape(-1), ref, ref_lse, "bf16", f"D128 split P={P}")
+
+
+# ---------------------------------------------------------------------------------------------
 # causal future-V perturbation (workshop checker)
 # ---------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("D", [64, 128])
