@@ -504,12 +504,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
 }
 
 // ---- host-side dispatch -------------------------------------------------------------------
-#ifndef FWD_WAVES
-#define FWD_WAVES(D) 4
-#endif
-#ifndef FWD_BN128
-#define FWD_BN128 64
-#endif
+// D = 128 runs eight waves (256 query rows) per workgroup, one workgroup per CU: each K/V tile
+// staged into LDS then serves twice as many queries as with four waves.  Smaller D run four
+// waves, two or more workgroups per CU.
+template <int D> constexpr int fwd_waves() { return D == 128 ? 8 : 4; }
 
 template <typename T, int D, int BN, bool MASK, bool SPLIT, int WAVES>
 static hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t s) {
@@ -522,7 +520,7 @@ static hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t s) {
 
 template <typename T, int D, int BN>
 static hipError_t launch_fwd_mask(const FwdParams& p, bool split, hipStream_t s) {
-  constexpr int W = FWD_WAVES(D);
+  constexpr int W = fwd_waves<D>();
   const bool mask = p.mask != nullptr;
   if (split) return mask ? launch_fwd_t<T, D, BN, true, true, W>(p, s) : launch_fwd_t<T, D, BN, false, true, W>(p, s);
   return mask ? launch_fwd_t<T, D, BN, true, false, W>(p, s) : launch_fwd_t<T, D, BN, false, false, W>(p, s);
@@ -534,7 +532,7 @@ static hipError_t launch_fwd_dtype(const FwdParams& p, int D, int BN, bool split
     case 16: return BN == 32 ? launch_fwd_mask<T, 16, 32>(p, split, s) : launch_fwd_mask<T, 16, 64>(p, split, s);
     case 32: return BN == 32 ? launch_fwd_mask<T, 32, 32>(p, split, s) : launch_fwd_mask<T, 32, 64>(p, split, s);
     case 64: return BN == 32 ? launch_fwd_mask<T, 64, 32>(p, split, s) : launch_fwd_mask<T, 64, 64>(p, split, s);
-    case 128: return launch_fwd_mask<T, 128, FWD_BN128>(p, split, s);
+    case 128: return launch_fwd_mask<T, 128, 64>(p, split, s);
     case 256: return launch_fwd_mask<T, 256, 64>(p, split, s);
   }
   return hipErrorInvalidValue;
