@@ -61,7 +61,7 @@ __device__ __forceinline__ int v_swz(int row) { return BITS ? 4 * ((row / RPB) &
 template <int S> using stage_t = std::integral_constant<int, S>;
 
 // WAVES waves of 32 query rows each; BN keys per tile.
-template <typename T, int D, int BN, bool MASK, bool SPLIT, int WAVES>
+template <typename T, int D, int BN, bool MASK, bool SPLIT, int WAVES, int NSTAGES>
 __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void attn_fwd_kernel(FwdParams p) {
   using E = elem<T>;
   constexpr int kBlockM = WAVES * kRowsPerWave;
@@ -80,13 +80,17 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   constexpr int DT = DP / 32;           // 32-row tiles of O^T
   static_assert(WAVES == 4 || WAVES == 8, "four or eight waves per workgroup");
   static_assert(TILE % 1024 == 0, "tile must be a whole number of 1 KiB wave loads");
-  // LDS: [K stage 0 | K stage 1 | V stage 0 | V stage 1].  Every operand read is a per-lane base
-  // plus a compile-time offset (block, key step, stage), which must fit the 16-bit DS offset.
-  constexpr int K_OFS = 0, V_OFS = 2 * TILE;
-  static_assert(TILE + (MT - 1) * 32 * RB < 65536, "K read offsets exceed the DS immediate");
-  static_assert(TILE + (BN - 1) * RB < 65536, "V read offsets exceed the DS immediate");
+  // LDS stages: tiles are loaded NSTAGE-1 ahead.  Three stages where one workgroup owns the CU
+  // (eight waves), two otherwise.
+  constexpr int NSTAGE = NSTAGES;
+  static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three LDS stages");
+  // LDS: [K stages | V stages].  Every operand read is a per-lane base plus a compile-time offset
+  // (block, key step, stage), which must fit the 16-bit DS offset.
+  constexpr int K_OFS = 0, V_OFS = NSTAGE * TILE;
+  static_assert((NSTAGE - 1) * TILE + (MT - 1) * 32 * RB < 65536, "K read offsets exceed the DS immediate");
+  static_assert((NSTAGE - 1) * TILE + (BN - 1) * RB < 65536, "V read offsets exceed the DS immediate");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NSTAGE * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -149,13 +153,17 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   const uint32_t vvo0 = (uint32_t)(((int64_t)row0 * row_stride + 8 * (ld_pc ^ v_swz<RPB, VSWZ_BITS>(row0))) * 2);
   const uint32_t jj_bytes = (uint32_t)((int64_t)WAVES * RPI * row_stride * 2);   // scalar step per jj
   const uint32_t tile_bytes = (uint32_t)((int64_t)BN * row_stride * 2);
+  // s_waitcnt immediate for "vmcnt <= the loads of one tile" (gfx9 encoding: vmcnt in bits 3:0
+  // and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima, i.e. not waited for)
+  constexpr int kTileLoads = 2 * PER_WAVE;
+  static_assert(NSTAGE == 2 || NT % WAVES == 0, "three stages need the same load count in every wave");
+  constexpr int kWaitAllButOneTile = (kTileLoads & 15) | ((kTileLoads >> 4) << 14) | (7 << 4) | (15 << 8);
   // the LDS destination goes to M0, which must be provably wave-uniform
   const int wave_lds = __builtin_amdgcn_readfirstlane(wave * 1024);
-  auto issue_tile = [&](int t, auto stage_c) {
-    constexpr int S = decltype(stage_c)::value;
+  auto issue_tile = [&](int t, int stage) {
     const int k0 = kbeg + t * BN;
-    uint8_t* kdst = lds + K_OFS + S * TILE + wave_lds;
-    uint8_t* vdst = lds + V_OFS + S * TILE + wave_lds;
+    uint8_t* kdst = lds + K_OFS + stage * TILE + wave_lds;
+    uint8_t* vdst = lds + V_OFS + stage * TILE + wave_lds;
     __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)k0 * row_stride), 0, tile_bytes, 0x00020000);
     __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)k0 * row_stride), 0, tile_bytes, 0x00020000);
     if (k0 + BN <= p.Nkv) {
@@ -253,10 +261,12 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
     constexpr int S = decltype(stage_c)::value;
     const int k0 = kbeg + t * BN;
     // tile t resident for every wave (its LDS-DMA loads are counted by vmcnt, which the
-    // barrier's own fence does not wait for); every wave done with tile t-1's stage
-    __builtin_amdgcn_s_waitcnt(0);
+    // barrier's own fence does not wait for; with three stages the loads of tile t+1, issued
+    // after it, may stay in flight); every wave done with tile t-1, whose stage is refilled next
+    if (NSTAGE == 3 && t + 1 < ntiles) __builtin_amdgcn_s_waitcnt(kWaitAllButOneTile);
+    else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < ntiles) issue_tile(t + 1, stage_t<S ^ 1>{});
+    if (t + NSTAGE - 1 < ntiles) issue_tile(t + NSTAGE - 1, (S + NSTAGE - 1) % NSTAGE);
 
     // wave-uniform decisions for this tile
     const bool future = p.causal && (k0 > q0 + kRowsPerWave - 1);   // no key visible to any row
@@ -453,11 +463,15 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   };
 #undef ATTN_PIN
 
-  if (ntiles > 0) issue_tile(0, stage_t<0>{});
-  // two tiles per iteration, so that the LDS stage of every operand read is a constant
-  for (int t = 0; t < ntiles; t += 2) {
+#pragma unroll
+  for (int i = 0; i < NSTAGE - 1; ++i)
+    if (i < ntiles) issue_tile(i, i);
+  // NSTAGE tiles per iteration, so that the LDS stage of every operand read is a constant
+  for (int t = 0; t < ntiles; t += NSTAGE) {
     do_tile(t, stage_t<0>{});
     if (t + 1 < ntiles) do_tile(t + 1, stage_t<1>{});
+    if constexpr (NSTAGE == 3)
+      if (t + 2 < ntiles) do_tile(t + 2, stage_t<2>{});
   }
 
   // ---- epilogue: finish the denominator over the lane pair, normalise, store
@@ -511,10 +525,11 @@ template <int D> constexpr int fwd_waves() { return D == 128 ? 8 : 4; }
 
 template <typename T, int D, int BN, bool MASK, bool SPLIT, int WAVES>
 static hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t s) {
+  constexpr int NSTAGES = WAVES == 8 ? 3 : 2;
   FwdParams p = p0;
   p.n_qblocks = (p.Nq + WAVES * kRowsPerWave - 1) / (WAVES * kRowsPerWave);
   dim3 grid((unsigned)((int64_t)p.n_qblocks * p.H * p.B * p.P));
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, MASK, SPLIT, WAVES>), grid, dim3(64 * WAVES), 0, s, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, MASK, SPLIT, WAVES, NSTAGES>), grid, dim3(64 * WAVES), 0, s, p);
   return hipGetLastError();
 }
 
