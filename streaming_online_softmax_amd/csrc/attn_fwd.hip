@@ -13,7 +13,7 @@
 // inside one wave): one workgroup of WAVES waves per (query block of 32*WAVES rows, head, batch,
 // partition); each wave owns 32 whole query rows and the block's full key range, so no
 // cross-wave exchange is ever needed.  The waves share the K and V tiles, which are staged
-// into LDS by direct global-to-LDS loads, two stages deep, one barrier per tile.
+// into LDS by direct global-to-LDS loads, two or three stages deep, one barrier per tile.
 //
 // Transposed products: the kernel computes S^T = K Q^T and O^T = V^T P^T.  In both
 // accumulators a lane owns one query COLUMN, so the per-query state (m, l, alpha) is one scalar
