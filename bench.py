@@ -8,8 +8,9 @@ One step is one pass over every kernel of the path, on resident synthetic inputs
     3. attn_combine      merge of that P=16 workspace into the bf16 output
 `value` is the prefill's throughput in TFLOP/s of algorithmic work (4*D per visible
 query-key pair, causal diagonal included); the decode and combine bandwidths are reported
-beside it, together with a decode sweep over P in {4, 8, 16, 37} and a combine measured on a
-workspace too large for the caches.  Every per-kernel time comes from HIP events recorded on the
+beside it, together with a decode sweep over P in {4, 8, 16, 37} (two launches, and the same
+work fused into one attn_fwd_splitk_fused launch) and a combine measured on a workspace too large
+for the caches.  Every per-kernel time comes from HIP events recorded on the
 stream the kernels are launched on, over the whole timed region.  Rank 0 prints one JSON line.
 """
 import argparse
@@ -210,6 +211,13 @@ def main():
                                  lambda: sa.attn_combine(op, lp, ob)], 10, 3)
             sweep[str(P)] = {"decode_ms": m[0], "decode_GB/s": decode_bytes(sd["B"], sd["H"], sd["Nkv"], sd["D"], P) / (m[0] * 1e-3) / 1e9,
                              "combine_ms": m[1], "combine_GB/s": combine_bytes(P, RH, sd["D"]) / (m[1] * 1e-3) / 1e9}
+            # the same producer and merge in one launch (attn_fwd_splitk_fused)
+            tk = torch.zeros(RH, dtype=torch.int32, device=dev)
+            fl_ = torch.empty((sd["B"], sd["H"]), dtype=torch.float32, device=dev)
+            _, mf = timed_events([lambda: sa.attn_fwd_splitk_fused(dq, dk, dv, P, op, lp, tk, ob, fl_)], 10, 3)
+            fb = decode_bytes(sd["B"], sd["H"], sd["Nkv"], sd["D"], P) + combine_bytes(P, RH, sd["D"])
+            sweep[str(P)].update({"fused_ms": mf[0], "fused_GB/s": fb / (mf[0] * 1e-3) / 1e9,
+                                  "two_launch_ms": m[0] + m[1]})
         extra["decode_sweep"] = sweep
         # ---- combine on a workspace larger than the caches (rows 8192, heads 32, depth 128) -
         Pc, rows_c = 16, 8192

@@ -99,6 +99,29 @@ int attn_fwd_splitk(const void* q, const void* k, const void* v, void* out, floa
                     float* lse_partial, int dtype, void* stream);
 
 /*
+ * attn_fwd_splitk_fused -- attn_fwd_splitk followed by the combine, in ONE launch (the CDNA4
+ *   counterpart of Modular MAX "fa4_splitk_combine"'s overlap of the combine with the producer's
+ *   tail).  Each (row-head, partition) workgroup writes its workspace entry as attn_fwd_splitk
+ *   does, makes it visible device-wide and increments tickets[rh]; the workgroup that takes the
+ *   last ticket merges the P entries with attn_combine's formulas, writes out / lse and resets
+ *   tickets[rh] to 0.  Every row-head runs on the bandwidth-bound decode kernel, so this is
+ *   meant for few-query (decode) shapes.
+ *   Arguments as attn_fwd_splitk, except:
+ *   out          REQUIRED, [B, Nq, H, D] of `dtype`.
+ *   lse          nullable; [B, Nq, H] float32, natural log.
+ *   tickets      REQUIRED, uint32 [B * Nq * H], 4-byte aligned, caller-owned.  It must hold 0 in
+ *                every entry before the first call (e.g. one hipMemset at allocation); a call that
+ *                runs to completion leaves it at 0 again, so it is reusable without clearing.
+ *                Two calls that overlap in time (different streams) must not share it.
+ *   Errors: ATTN_E_WORKSPACE if o_partial, lse_partial or tickets is NULL; otherwise as
+ *   attn_fwd_splitk and attn_combine.
+ */
+int attn_fwd_splitk_fused(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                          int H, int Nq, int Nkv, int D, int causal, const uint8_t* mask, int P,
+                          float* o_partial, float* lse_partial, uint32_t* tickets, int dtype,
+                          void* stream);
+
+/*
  * attn_combine -- merge a split-K workspace (Modular MAX "fa4_splitk_combine"):
  *   for each row-head rh of rows*heads:  m* = max_p lse_p;  G = log2(sum_p 2^(lse_p - m*)) + m*;
  *   scale_p = 2^(lse_p - G);  out[rh, d] = sum_p scale_p * o_partial[p, rh, d].

@@ -8,11 +8,14 @@ Entry points (same names as the C ABI in include/attn.h):
     attn_fwd(q, k, v, out, lse=None, causal=False, mask=None, block_n=0, stream=None)
     attn_fwd_splitk(q, k, v, P, o_partial, lse_partial, out=None, lse=None, causal=False,
                     mask=None, stream=None)
+    attn_fwd_splitk_fused(q, k, v, P, o_partial, lse_partial, tickets, out, lse=None, causal=False,
+                          mask=None, stream=None)
     attn_combine(o_partial, lse_partial, out, lse_out=None, stream=None)
     attn_last_error(), attn_abi_version()
 Tensors are torch tensors on the GPU, contiguous, laid out as the header states
-(q/out [B, Nq, H, D]; k/v [B, Nkv, H, D]; o_partial [P, B*Nq, H, D]; lse_partial [P, B*Nq, H]).
-Allocating helpers fwd(), splitk() and combine() return fresh outputs.
+(q/out [B, Nq, H, D]; k/v [B, Nkv, H, D]; o_partial [P, B*Nq, H, D]; lse_partial [P, B*Nq, H];
+tickets int32 [B*Nq*H], zero before the first call and left zero by every call).
+Allocating helpers fwd(), splitk(), splitk_fused() and combine() return fresh outputs.
 """
 import ctypes
 import os
@@ -63,6 +66,8 @@ def _load():
     L.attn_fwd.restype = i32
     L.attn_fwd_splitk.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp, vp, i32, vp]
     L.attn_fwd_splitk.restype = i32
+    L.attn_fwd_splitk_fused.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp, vp, vp, i32, vp]
+    L.attn_fwd_splitk_fused.restype = i32
     L.attn_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     L.attn_combine.restype = i32
     L.attn_fwd_ex.argtypes = [ctypes.POINTER(FwdArgs), vp]
@@ -132,6 +137,15 @@ def attn_fwd_splitk(q, k, v, P, o_partial, lse_partial, out=None, lse=None, caus
                                _dtype_code(q), _stream(stream)))
 
 
+def attn_fwd_splitk_fused(q, k, v, P, o_partial, lse_partial, tickets, out, lse=None, causal=False,
+                          mask=None, stream=None):
+    B, Nq, H, D = q.shape
+    Nkv = k.shape[1]
+    _check(lib().attn_fwd_splitk_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nkv, D,
+                                     int(causal), _ptr(mask), int(P), _ptr(o_partial), _ptr(lse_partial),
+                                     _ptr(tickets), _dtype_code(q), _stream(stream)))
+
+
 def attn_combine(o_partial, lse_partial, out, lse_out=None, stream=None):
     P = o_partial.shape[0]
     depth = o_partial.shape[-1]
@@ -164,6 +178,21 @@ def splitk(q, k, v, P, causal=False, mask=None, combine=True):
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     attn_fwd_splitk(q, k, v, P, o_p, l_p, out=out, lse=lse, causal=causal, mask=mask)
     return o_p, l_p, out, lse
+
+
+def tickets(q):
+    """A zeroed ticket array for attn_fwd_splitk_fused (reusable: every call leaves it zero)."""
+    B, Nq, H, _ = q.shape
+    return torch.zeros(B * Nq * H, dtype=torch.int32, device=q.device)
+
+
+def splitk_fused(q, k, v, P, causal=False, mask=None, tk=None):
+    o_p, l_p = workspace(q, P)
+    tk = tickets(q) if tk is None else tk
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn_fwd_splitk_fused(q, k, v, P, o_p, l_p, tk, out, lse=lse, causal=causal, mask=mask)
+    return out, lse, o_p, l_p
 
 
 def combine(o_partial, lse_partial, out_dtype=torch.float32):

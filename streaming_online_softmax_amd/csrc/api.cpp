@@ -156,7 +156,7 @@ int attn_fwd_splitk(const void* q, const void* k, const void* v, void* out, floa
     attn::DecodeParams p{};
     p.q = q; p.k = k; p.v = v; p.o_partial = o_partial; p.lse_partial = lse_partial; p.mask = mask;
     p.B = B; p.H = H; p.Nq = Nq; p.Nkv = Nkv; p.causal = causal; p.P = P; p.chunk = chunk; p.scale_log2 = c;
-    rc = hip_status(attn::launch_decode(p, dtype, D, s), "attn_fwd_splitk decode launch");
+    rc = hip_status(attn::launch_decode(p, dtype, D, false, s), "attn_fwd_splitk decode launch");
   } else {
     const int64_t nqb = ((int64_t)Nq + attn::fwd_block_m() - 1) / attn::fwd_block_m();
     if (nqb * H * B * P > 0x7fffffffLL) return fail(ATTN_E_SHAPE, "grid too large");
@@ -170,6 +170,30 @@ int attn_fwd_splitk(const void* q, const void* k, const void* v, void* out, floa
   }
   if (rc || !out) return rc;
   return do_combine(o_partial, lse_partial, out, lse, P, B * Nq, H, D, dtype, s);
+}
+
+int attn_fwd_splitk_fused(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                          int H, int Nq, int Nkv, int D, int causal, const uint8_t* mask, int P,
+                          float* o_partial, float* lse_partial, uint32_t* tickets, int dtype,
+                          void* stream) {
+  int rc = check_qkv(q, k, v, B, H, Nq, Nkv, D, causal, dtype);
+  if (rc) return rc;
+  if (P < 1) return fail(ATTN_E_SHAPE, "P must be >= 1 (got %d)", P);
+  if (P > ATTN_P_MAX) return fail(ATTN_E_UNSUPPORTED, "P=%d exceeds ATTN_P_MAX=%d", P, ATTN_P_MAX);
+  if (!o_partial || !lse_partial || !tickets) return fail(ATTN_E_WORKSPACE, "o_partial, lse_partial and tickets are required");
+  if (!aligned(tickets, 4)) return fail(ATTN_E_ALIGN, "tickets must be 4-byte aligned");
+  const int64_t RH = (int64_t)B * Nq * H;
+  if (RH > 0x7fffffffLL) return fail(ATTN_E_SHAPE, "B*Nq*H exceeds 2^31-1");
+  if (RH * P > 0x7fffffffLL) return fail(ATTN_E_SHAPE, "grid too large");
+  rc = check_combine(o_partial, lse_partial, out, lse, P, B * Nq, H, D, dtype);
+  if (rc) return rc;
+  attn::DecodeParams p{};
+  p.q = q; p.k = k; p.v = v; p.o_partial = o_partial; p.lse_partial = lse_partial; p.mask = mask;
+  p.B = B; p.H = H; p.Nq = Nq; p.Nkv = Nkv; p.causal = causal; p.P = P;
+  p.chunk = (int)(((int64_t)Nkv + P - 1) / P);
+  p.scale_log2 = scale_log2(D);
+  p.out = out; p.lse = lse; p.tickets = tickets;
+  return hip_status(attn::launch_decode(p, dtype, D, true, (hipStream_t)stream), "attn_fwd_splitk_fused launch");
 }
 
 int attn_combine(const float* o_partial, const float* lse_partial, void* out, float* lse_out, int P,

@@ -11,12 +11,18 @@
 // step in log2 units; the four waves of a workgroup hold independent states over interleaved
 // key chunks and are merged once at the end with the same rescale rule (Tylo.jl "Streaming
 // attention and online state", section "Online statistics", merge of two summaries).
+//
+// Fused form (FUSED): after writing its workspace entry, each workgroup takes a ticket for its
+// row-head; the one that takes the last ticket merges all P entries with the LSE-weighted
+// combine (Modular MAX "fa4_splitk_combine", per-row-head formulas) and writes the output, so
+// decode is one launch instead of producer + combine.  This is the one-GPU stand-in for the
+// page's programmatic launch overlap of the combine with the producer's tail.
 #include "device.h"
 #include "launch.h"
 
 namespace attn {
 
-template <typename T, int D, bool MASK>
+template <typename T, int D, bool MASK, bool FUSED>
 __global__ __launch_bounds__(256) void attn_decode_kernel(DecodeParams p) {
   using E = elem<T>;
   constexpr int LPK = D / 8;        // lanes per key row (16 bytes each)
@@ -143,30 +149,86 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecodeParams p) {
     p.o_partial[prh * D + d] = acc * inv;
   }
   if (tid == 0) p.lse_partial[prh] = L == 0.f ? kNegInf : M_use + log2f(L);
+
+  if constexpr (FUSED) {
+    // ---- publish this partition, then count it.  Every thread makes its own workspace
+    //      stores visible device-wide before the barrier; one thread then takes the ticket.
+    __shared__ int sm_last;
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t t = __hip_atomic_fetch_add(p.tickets + rh, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      sm_last = (t == (uint32_t)p.P - 1u);
+    }
+    __syncthreads();
+    if (!sm_last) return;
+    // ---- last partition of this row-head: see every other workgroup's entries, then merge
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __shared__ float sc_tab[ATTN_P_MAX_DEV];
+    __shared__ float red[2][4];
+    __shared__ __attribute__((aligned(16))) float part_acc[1024];
+    const int64_t RH = (int64_t)p.B * p.Nq * p.H;
+    // LSE phase: thread t holds partition t (P <= 256 = threads)
+    const float lsv = tid < p.P ? p.lse_partial[(int64_t)tid * RH + rh] : kNegInf;
+    float wm = across_groups_max<1>(lsv);
+    if (lane == 0) red[0][wave] = wm;
+    __syncthreads();
+    const float mx = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    float e = (lsv == kNegInf) ? 0.f : fast_exp2(lsv - mx);
+    e = group_sum<64>(e);
+    if (lane == 0) red[1][wave] = e;
+    __syncthreads();
+    const float sum = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+    const bool empty = (mx == kNegInf);
+    const float Gl = empty ? kNegInf : log2f(sum) + mx;
+    if (tid < p.P) sc_tab[tid] = (empty || lsv == kNegInf) ? 0.f : fast_exp2(lsv - Gl);
+    __syncthreads();
+    // weighted sum: thread -> (4-element slice c, partition group pg); groups then folded in LDS
+    constexpr int NC = D / 4, NG = 256 / NC;
+    const int c4 = tid % NC, pg = tid / NC;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float* src = p.o_partial + rh * D + 4 * c4;
+    for (int pp = pg; pp < p.P; pp += NG) {
+      const float sp = sc_tab[pp];
+      if (sp != 0.f) acc += sp * *reinterpret_cast<const f32x4*>(src + (int64_t)pp * RH * D);   // empty adds nothing
+    }
+    *reinterpret_cast<f32x4*>(part_acc + 4 * tid) = acc;
+    __syncthreads();
+    if (tid < NC) {
+      f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int g2 = 0; g2 < NG; ++g2) r += *reinterpret_cast<const f32x4*>(part_acc + 4 * (g2 * NC + tid));
+      *reinterpret_cast<u32x2*>((uint16_t*)p.out + rh * D + 4 * tid) = u32x2{E::pack2(r[0], r[1]), E::pack2(r[2], r[3])};
+    }
+    if (tid == 0) {
+      if (p.lse) p.lse[rh] = empty ? kNegInf : Gl * kLn2;
+      __hip_atomic_store(p.tickets + rh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
+    }
+  }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool FUSED>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
   dim3 grid((unsigned)((int64_t)p.B * p.Nq * p.H * p.P));
-  if (p.mask) hipLaunchKernelGGL((attn_decode_kernel<T, D, true>), grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((attn_decode_kernel<T, D, false>), grid, dim3(256), 0, s, p);
+  if (p.mask) hipLaunchKernelGGL((attn_decode_kernel<T, D, true, FUSED>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((attn_decode_kernel<T, D, false, FUSED>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool FUSED>
 static hipError_t launch_decode_dtype(const DecodeParams& p, int D, hipStream_t s) {
   switch (D) {
-    case 16: return launch_decode_t<T, 16>(p, s);
-    case 32: return launch_decode_t<T, 32>(p, s);
-    case 64: return launch_decode_t<T, 64>(p, s);
-    case 128: return launch_decode_t<T, 128>(p, s);
-    case 256: return launch_decode_t<T, 256>(p, s);
+    case 16: return launch_decode_t<T, 16, FUSED>(p, s);
+    case 32: return launch_decode_t<T, 32, FUSED>(p, s);
+    case 64: return launch_decode_t<T, 64, FUSED>(p, s);
+    case 128: return launch_decode_t<T, 128, FUSED>(p, s);
+    case 256: return launch_decode_t<T, 256, FUSED>(p, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const DecodeParams& p, int dtype, int D, hipStream_t s) {
-  return dtype == 0 ? launch_decode_dtype<bf16_t>(p, D, s) : launch_decode_dtype<f16_t>(p, D, s);
+hipError_t launch_decode(const DecodeParams& p, int dtype, int D, bool fused, hipStream_t s) {
+  if (fused) return dtype == 0 ? launch_decode_dtype<bf16_t, true>(p, D, s) : launch_decode_dtype<f16_t, true>(p, D, s);
+  return dtype == 0 ? launch_decode_dtype<bf16_t, false>(p, D, s) : launch_decode_dtype<f16_t, false>(p, D, s);
 }
 
 }  // namespace attn

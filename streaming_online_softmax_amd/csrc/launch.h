@@ -39,6 +39,11 @@ struct DecodeParams {
   int P;
   int chunk;
   float scale_log2;
+  // fused combine (attn_fwd_splitk_fused): the last workgroup of each row-head merges the
+  // workspace into out / lse; tickets[rh] counts finished partitions and is returned to 0
+  void* out;            // [B, Nq, H, D] input dtype
+  float* lse;           // [B, Nq, H] natural log, nullable
+  uint32_t* tickets;    // [B * Nq * H], zero on entry and on exit
 };
 
 // LSE-weighted combine of a split-K workspace.
@@ -52,7 +57,7 @@ struct CombineParams {
 };
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int BN, bool split, hipStream_t s);
-hipError_t launch_decode(const DecodeParams& p, int dtype, int D, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int dtype, int D, bool fused, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, int depth, int out_dtype, hipStream_t s);
 int fwd_block_m();
 

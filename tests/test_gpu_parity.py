@@ -232,6 +232,63 @@ def test_decode_empty_partitions(sa):
     _compare(out.reshape(6, -1), lse.reshape(-1), ref, ref_lse, "bf16", "decode P>Nkv")
 
 
+@pytest.mark.parametrize("P", [4, 8, 16, 37])
+def test_decode_fused_full_size(sa, decode_data, P):
+    """attn_fwd_splitk_fused: one launch; the workspace equals the unfused producer's bit for
+    bit (same code), the merged output matches the two-launch path within one bf16 rounding of
+    each (their FP32 merge orders differ) and the oracle on sampled rows; tickets end at 0."""
+    s = si.DECODE
+    q, k, v, qd, kd, vd = decode_data
+    tk = sa.tickets(qd)
+    out, lse, o_p, l_p = sa.splitk_fused(qd, kd, vd, P, tk=tk)
+    o_u, l_u, out_u, lse_u = sa.splitk(qd, kd, vd, P)
+    torch.cuda.synchronize()
+    assert int(tk.abs().sum()) == 0
+    assert torch.equal(o_p, o_u) and torch.equal(l_p, l_u)
+    RH = s["B"] * s["H"]
+    a, b = out.float().reshape(RH, -1), out_u.float().reshape(RH, -1)
+    assert bool(((a - b).abs() <= 2.0 ** -8 * torch.maximum(a.abs(), b.abs()) + 1e-6).all())
+    assert torch.allclose(lse, lse_u, rtol=1e-6, atol=1e-6)
+    rows = np.unique(si.rng_for(87, P).integers(0, RH, 48))
+    ref, ref_lse = oracle.attn_dense(q, k, v, rows=rows)
+    rt = torch.from_numpy(rows).to(DEV)
+    _compare(out.reshape(RH, -1)[rt], lse.reshape(-1)[rt], ref, ref_lse, "bf16", f"fused P={P}")
+
+
+def test_decode_fused_reuses_tickets(sa):
+    """Two fused calls in a row on one ticket array, the second smaller (fewer partitions, other
+    data, fp16): both match the oracle and the tickets are 0 after each."""
+    rng = si.rng_for(88, 0)
+    tk = torch.zeros(2 * 1 * 8, dtype=torch.int32, device=DEV)
+    for P, n, dt in ((13, 3000, "bf16"), (5, 700, "f16")):
+        q, k, v = (si.cast(x, dt) for x in si.draw_qkv(rng, (2, 1, 8, 64), (2, n, 8, 64)))
+        out, lse, _, _ = sa.splitk_fused(q.to(DEV), k.to(DEV), v.to(DEV), P, tk=tk)
+        torch.cuda.synchronize()
+        assert int(tk.abs().sum()) == 0
+        ref, ref_lse = oracle.attn_dense(q, k, v)
+        _compare(out.reshape(16, -1), lse.reshape(-1), ref, ref_lse, dt, f"fused P={P} n={n}")
+
+
+def test_decode_fused_empty_and_masked(sa):
+    """Fused decode with more partitions than keys, and with a byte mask that hides every key of
+    one row-head's query (output 0, lse -inf), and with a few queries per head (Nq = 3)."""
+    rng = si.rng_for(89, 0)
+    q, k, v = (si.cast(x, "bf16") for x in si.draw_qkv(rng, (2, 1, 3, 128), (2, 17, 3, 128)))
+    out, lse, _, _ = sa.splitk_fused(q.to(DEV), k.to(DEV), v.to(DEV), 37)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.attn_dense(q, k, v)
+    _compare(out.reshape(6, -1), lse.reshape(-1), ref, ref_lse, "bf16", "fused P>Nkv")
+    Nq, Nkv = 3, 500
+    q, k, v = (si.cast(x, "bf16") for x in si.draw_qkv(rng, (1, Nq, 4, 64), (1, Nkv, 4, 64)))
+    mask, _ = si.bernoulli_mask(rng, Nq, Nkv, 0)
+    mask[1, :] = 0
+    out, lse, _, _ = sa.splitk_fused(q.to(DEV), k.to(DEV), v.to(DEV), 6, mask=torch.from_numpy(mask).to(DEV))
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.attn_dense(q, k, v, mask=mask)
+    _compare(out.reshape(Nq * 4, -1), lse.reshape(-1), ref, ref_lse, "bf16", "fused masked Nq=3")
+    assert bool((out[0, 1] == 0).all()) and bool(torch.isneginf(lse[0, 1]).all())
+
+
 @pytest.mark.parametrize("P", [1, 3, 7])
 def test_square_causal_split_matches_unsplit(sa, P):
     """Square causal shapes through the matrix-core split path.  Here |O| reaches ~3 and the
@@ -342,5 +399,9 @@ def test_reject_paths_write_nothing(sa):
     q48 = torch.zeros(1, 64, 2, 48, device=DEV, dtype=torch.bfloat16)
     with pytest.raises(sa.AttnError):
         sa.attn_fwd(q48, q48, q48, torch.zeros_like(q48))
+    q1 = q[:, :1]
+    with pytest.raises(sa.AttnError) as e:   # tickets are required
+        sa.attn_fwd_splitk_fused(q1, q, q, 4, o_p, l_p, None, torch.zeros_like(q1))
+    assert e.value.code == 5
     torch.cuda.synchronize()
     assert bool((out == 7.0).all()) and bool((o_p == 7.0).all()) and bool((l_p == 7.0).all())
