@@ -22,6 +22,17 @@
 
 namespace attn {
 
+// Workspace access.  The fused form publishes entries across workgroups of one launch, which
+// may run on different XCDs: it uses device-coherent (agent-scope) stores and loads.
+template <bool COHERENT>
+__device__ __forceinline__ void put_ws(float* a, float x) {
+  if constexpr (COHERENT) __hip_atomic_store(a, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *a = x;
+}
+__device__ __forceinline__ float get_ws(const float* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <typename T, int D, bool MASK, bool FUSED>
 __global__ __launch_bounds__(256) void attn_decode_kernel(DecodeParams p) {
   using E = elem<T>;
@@ -146,30 +157,37 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecodeParams p) {
     float acc = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) acc = fmaf(aw[w], sm_o[w][d], acc);
-    p.o_partial[prh * D + d] = acc * inv;
+    put_ws<FUSED>(p.o_partial + prh * D + d, acc * inv);
   }
-  if (tid == 0) p.lse_partial[prh] = L == 0.f ? kNegInf : M_use + log2f(L);
+  if (tid == 0) put_ws<FUSED>(p.lse_partial + prh, L == 0.f ? kNegInf : M_use + log2f(L));
 
   if constexpr (FUSED) {
-    // ---- publish this partition, then count it.  Every thread makes its own workspace
-    //      stores visible device-wide before the barrier; one thread then takes the ticket.
+    // ---- publish this partition, then count it.  The workspace entries above were written with
+    //      device-coherent stores (they bypass the per-XCD L2s, which are not coherent with one
+    //      another); each thread waits until its stores have completed, the barrier gathers the
+    //      workgroup, and one thread takes the ticket with a device-coherent atomic.  A workgroup
+    //      that draws the last ticket was therefore preceded by every other partition's completed
+    //      stores, and reads them back with device-coherent loads.  No cache-wide write-back or
+    //      invalidate is needed (an agent-scope release/acquire fence would do both, in every
+    //      workgroup, and costs more than the whole combine).
     __shared__ int sm_last;
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-      const uint32_t t = __hip_atomic_fetch_add(p.tickets + rh, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t t = __hip_atomic_fetch_add(p.tickets + rh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       sm_last = (t == (uint32_t)p.P - 1u);
     }
     __syncthreads();
     if (!sm_last) return;
-    // ---- last partition of this row-head: see every other workgroup's entries, then merge
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // ---- last partition of this row-head: merge the P entries
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     __shared__ float sc_tab[ATTN_P_MAX_DEV];
     __shared__ float red[2][4];
     __shared__ __attribute__((aligned(16))) float part_acc[1024];
     const int64_t RH = (int64_t)p.B * p.Nq * p.H;
     // LSE phase: thread t holds partition t (P <= 256 = threads)
-    const float lsv = tid < p.P ? p.lse_partial[(int64_t)tid * RH + rh] : kNegInf;
+    const float lsv = tid < p.P ? get_ws(p.lse_partial + (int64_t)tid * RH + rh) : kNegInf;
     float wm = across_groups_max<1>(lsv);
     if (lane == 0) red[0][wave] = wm;
     __syncthreads();
@@ -190,7 +208,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecodeParams p) {
     const float* src = p.o_partial + rh * D + 4 * c4;
     for (int pp = pg; pp < p.P; pp += NG) {
       const float sp = sc_tab[pp];
-      if (sp != 0.f) acc += sp * *reinterpret_cast<const f32x4*>(src + (int64_t)pp * RH * D);   // empty adds nothing
+      if (sp != 0.f) {   // an empty partition adds nothing
+        const float* e4 = src + (int64_t)pp * RH * D;
+        acc += sp * f32x4{get_ws(e4), get_ws(e4 + 1), get_ws(e4 + 2), get_ws(e4 + 3)};
+      }
     }
     *reinterpret_cast<f32x4*>(part_acc + 4 * tid) = acc;
     __syncthreads();

@@ -235,8 +235,9 @@ def test_decode_empty_partitions(sa):
 @pytest.mark.parametrize("P", [4, 8, 16, 37])
 def test_decode_fused_full_size(sa, decode_data, P):
     """attn_fwd_splitk_fused: one launch; the workspace equals the unfused producer's bit for
-    bit (same code), the merged output matches the two-launch path within one bf16 rounding of
-    each (their FP32 merge orders differ) and the oracle on sampled rows; tickets end at 0."""
+    bit (same code); the merged output matches the two-launch path to one bf16 unit in the last
+    place (their FP32 merge orders differ, so the two FP32 values may round to neighbouring bf16
+    numbers) and the oracle on sampled rows; tickets end at 0."""
     s = si.DECODE
     q, k, v, qd, kd, vd = decode_data
     tk = sa.tickets(qd)
@@ -246,8 +247,11 @@ def test_decode_fused_full_size(sa, decode_data, P):
     assert int(tk.abs().sum()) == 0
     assert torch.equal(o_p, o_u) and torch.equal(l_p, l_u)
     RH = s["B"] * s["H"]
-    a, b = out.float().reshape(RH, -1), out_u.float().reshape(RH, -1)
-    assert bool(((a - b).abs() <= 2.0 ** -8 * torch.maximum(a.abs(), b.abs()) + 1e-6).all())
+    a, b = out.reshape(-1), out_u.reshape(-1)
+    same_sign = torch.signbit(a.float()) == torch.signbit(b.float())
+    ulps = (a.view(torch.int16).int() - b.view(torch.int16).int()).abs()
+    assert bool((same_sign & (ulps <= 1)).all()), f"max {int(ulps.max())} bf16 ulps apart"
+    assert int((ulps > 0).sum()) < a.numel() // 100
     assert torch.allclose(lse, lse_u, rtol=1e-6, atol=1e-6)
     rows = np.unique(si.rng_for(87, P).integers(0, RH, 48))
     ref, ref_lse = oracle.attn_dense(q, k, v, rows=rows)
