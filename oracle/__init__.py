@@ -66,6 +66,8 @@ def lib():
         L.oracle_round_array.argtypes = [vp, i64, i32, vp]
         L.oracle_round_array.restype = None
         L.oracle_decode.argtypes = [vp, i32, i64, dp]
+        L.oracle_softmax_rows.argtypes = [vp, i32, i64, i64, dp]
+        L.oracle_softmax_rows.restype = None
         L.oracle_decode.restype = None
         L.oracle_num_threads.restype = i32
         _lib = L
@@ -203,6 +205,18 @@ def splitk(q, k, v, P, causal=False, mask=None, rows=None):
     if rc:
         raise ValueError("oracle_splitk failed")
     return o_p, l_p
+
+
+def softmax_rows(x):
+    """O5. Row softmax of the last axis with the all-masked conventions (-inf = masked; an
+    all-masked row gives zeros).  x: float32 / bfloat16 / float16 tensor or float32 array.
+    Returns float64 array of x's shape."""
+    x = _as_cpu_tensor(x)
+    n = x.shape[-1]
+    rows = x.numel() // n if n else 0
+    y = np.zeros(tuple(x.shape), np.float64)
+    lib().oracle_softmax_rows(_ptr(x), _dtype_code(x), rows, n, _ptr(y))
+    return y
 
 
 def round_bits(x, target):

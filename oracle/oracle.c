@@ -405,6 +405,34 @@ int oracle_splitk(const void* q, const void* k, const void* v, int dt, const uin
   return 0;
 }
 
+/* ---------------------------------------------------------------------------------------------
+ * O5. Row softmax with the all-masked conventions ([TR] "Worked softmax"): per row of n logits
+ *   m = max_j x_j;  shift(x, m) = (m == -inf) ? -inf : x - m;  w_j = exp(shift(x_j, m));
+ *   s = sum_j w_j;  y_j = (s == 0) ? 0 : w_j / s.
+ * A logit of -inf is a masked entry (weight 0); a row of only -inf gives all zeros.  x is a
+ * row-major [rows, n] array of float32, bfloat16 or float16; y is [rows, n] double.
+ * ------------------------------------------------------------------------------------------- */
+static double shift_logit(double x, double m) { return m == -INFINITY ? -INFINITY : x - m; }
+static double normalize_weight(double w, double s) { return s == 0.0 ? 0.0 : w / s; }
+
+void oracle_softmax_rows(const void* x, int dtype, int64_t rows, int64_t n, double* y) {
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t r = 0; r < rows; ++r) {
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) {
+      double v = load_elem(x, r * n + j, dtype);
+      if (v > m) m = v;
+    }
+    double s = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+      double w = exp(shift_logit(load_elem(x, r * n + j, dtype), m));
+      y[r * n + j] = w;
+      s += w;
+    }
+    for (int64_t j = 0; j < n; ++j) y[r * n + j] = normalize_weight(y[r * n + j], s);
+  }
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -446,3 +446,74 @@ def test_decode_every_pattern():
         assert np.array_equal(np.isnan(got), nan)
         np.testing.assert_array_equal(got[~nan], ref[~nan])
         np.testing.assert_array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+# ------------------------------------------------------------------------------------------
+# O5: standalone row softmax (Tylo "Register fragments and logical axes", "Worked softmax";
+# Tylo "Streaming attention and online state", "Online statistics")
+# ------------------------------------------------------------------------------------------
+def test_row_softmax_state_example():
+    """The SoftmaxState example printed on the page: scores (0, 0) normalise to (0.5, 0.5)."""
+    g = _golden("softmax_state_example.json")
+    y = oracle.softmax_rows(np.array([g["scores"]], np.float32))
+    assert y[0].tolist() == g["normalized_weights"]
+
+
+def test_row_softmax_all_masked_conventions():
+    """'Worked softmax': -inf logits get weight exactly 0, the other entries are the softmax of
+    the visible ones alone, and a row with every logit -inf normalises to zeros (not NaN)."""
+    rng = si.rng_for(90, 0)
+    x = rng.standard_normal((6, 37)).astype(np.float32)
+    x[0, :] = -np.inf
+    x[1, 5] = -np.inf
+    x[2, ::2] = -np.inf
+    x[3, 1:] = -np.inf
+    y = oracle.softmax_rows(x)
+    assert np.all(y[0] == 0.0)
+    assert y[3, 0] == 1.0 and np.all(y[3, 1:] == 0.0)
+    for r in (1, 2, 4, 5):
+        vis = np.isfinite(x[r])
+        assert np.all(y[r, ~vis] == 0.0)
+        w = [math.exp(float(t) - max(x[r, vis].astype(np.float64))) for t in x[r, vis].astype(np.float64)]
+        s = math.fsum(w)
+        np.testing.assert_allclose(y[r, vis], [t / s for t in w], rtol=1e-14, atol=0)
+
+
+def test_row_softmax_closed_forms():
+    """Uniform logits give 1/n; two logits give the logistic function; adding a constant to a
+    row (a power of two, exact in float32) or permuting its entries changes nothing but the
+    order."""
+    for n in (1, 2, 3, 64, 1000):
+        y = oracle.softmax_rows(np.full((2, n), 1.75, np.float32))
+        np.testing.assert_allclose(y, 1.0 / n, rtol=1e-15)
+    a, b = 0.25, -1.5
+    y = oracle.softmax_rows(np.array([[a, b]], np.float32))[0]
+    np.testing.assert_allclose(y, [1 / (1 + math.exp(b - a)), 1 / (1 + math.exp(a - b))], rtol=1e-15)
+    rng = si.rng_for(90, 1)
+    x = (np.round(rng.standard_normal((4, 300)) * 1024) / 1024).astype(np.float32)   # x + 64 exact
+    y = oracle.softmax_rows(x)
+    np.testing.assert_allclose(oracle.softmax_rows(x + np.float32(64.0)), y, rtol=1e-12)
+    perm = rng.permutation(300)
+    np.testing.assert_allclose(oracle.softmax_rows(x[:, perm]), y[:, perm], rtol=1e-15)
+
+
+def test_row_softmax_matches_library_routine():
+    """The textbook definition as an independent library computes it (scipy.special.softmax,
+    float64), on normal and x30 large logits: natural exponent, max-shifted, rows sum to 1."""
+    from scipy.special import softmax as sp_softmax
+    rng = si.rng_for(90, 2)
+    for scale in (1.0, 30.0):
+        x = (rng.standard_normal((8, 513)) * scale).astype(np.float32)
+        y = oracle.softmax_rows(x)
+        np.testing.assert_allclose(y, sp_softmax(x.astype(np.float64), axis=1), rtol=1e-12, atol=1e-300)
+        np.testing.assert_allclose(y.sum(axis=1), 1.0, rtol=1e-13)
+
+
+def test_row_softmax_reads_16_bit_inputs_exactly():
+    """bfloat16 and float16 logits are widened exactly: the result equals the float32 path on
+    the same (representable) values."""
+    rng = si.rng_for(90, 3)
+    x = rng.standard_normal((3, 77)).astype(np.float32)
+    for dt in ("bf16", "f16"):
+        xt = si.cast(x, dt)
+        np.testing.assert_array_equal(oracle.softmax_rows(xt), oracle.softmax_rows(xt.float()))
