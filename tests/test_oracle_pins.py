@@ -494,7 +494,7 @@ def test_row_softmax_closed_forms():
     y = oracle.softmax_rows(x)
     np.testing.assert_allclose(oracle.softmax_rows(x + np.float32(64.0)), y, rtol=1e-12)
     perm = rng.permutation(300)
-    np.testing.assert_allclose(oracle.softmax_rows(x[:, perm]), y[:, perm], rtol=1e-15)
+    np.testing.assert_allclose(oracle.softmax_rows(x[:, perm]), y[:, perm], rtol=1e-13)   # sum order
 
 
 def test_row_softmax_matches_library_routine():
