@@ -10,7 +10,8 @@ One step is one pass over every kernel of the path, on resident synthetic inputs
 query-key pair, causal diagonal included); the decode and combine bandwidths are reported
 beside it, together with a decode sweep over P in {4, 8, 16, 37} (two launches, and the same
 work fused into one attn_fwd_splitk_fused launch) and a combine measured on a workspace too large
-for the caches.  Every per-kernel time comes from HIP events recorded on the
+for the caches, and the standalone row softmax (three methods) on 32768 x 4096 and 4096 x 32768
+fp32 rows.  Every per-kernel time comes from HIP events recorded on the
 stream the kernels are launched on, over the whole timed region.  Rank 0 prints one JSON line.
 """
 import argparse
@@ -43,6 +44,25 @@ def decode_bytes(B, H, Nkv, D, P):
     q = B * H * D * 2
     egress = P * B * H * (D + 1) * 4             # o_partial + lse_partial, fp32
     return kv + q + egress
+
+
+def softmax_figures(sa, dev, steps=10, warmup=3):
+    """GB/s of algorithmic bytes (read x once, write y once) for each method."""
+    res = {}
+    for w in (si.SOFTMAX, si.SOFTMAX_WIDE):
+        x = torch.from_numpy(si.softmax_inputs(w["rows"], w["n"], case=0)).to(dev)
+        y = torch.empty_like(x)
+        nbytes = 2 * x.numel() * 4
+        fig = {}
+        for name, m in (("streaming", 0), ("registers", 1), ("three_pass", 2)):
+            if m == 1 and w["n"] > 4096:
+                continue
+            _, ms = timed_events([lambda: sa.attn_softmax_rows(x, y, m)], steps, warmup)
+            fig[name] = {"ms": ms[0], "GB/s": nbytes / (ms[0] * 1e-3) / 1e9,
+                         "hbm_frac": nbytes / (ms[0] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        res[w["name"]] = fig
+        del x, y
+    return res
 
 
 def combine_bytes(P, RH, D, out_elem=2):
@@ -134,7 +154,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "combine", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "combine", "copy", "softmax"], default=None,
                     help="time a single kernel (for profiler runs); 'copy' times a plain 1 GiB device "
                          "copy, the calibration for the HBM byte counters")
     args = ap.parse_args()
@@ -154,6 +174,9 @@ def main():
         _, ms = timed_events([lambda: dst.copy_(src)], args.steps, args.warmup)
         print(json.dumps({"calibration": "device copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
                           "ms": ms[0], "GB/s": 2 * (1 << 30) / (ms[0] * 1e-3) / 1e9}), flush=True)
+        return
+    if args.only == "softmax":
+        print(json.dumps({"softmax": softmax_figures(sa, dev, args.steps, args.warmup)}), flush=True)
         return
     # ---- inputs (seeded, synthetic, resident in HBM before timing) -----------------------
     sp = si.PREFILL
@@ -230,6 +253,8 @@ def main():
                                   "GB/s": cb / (m[0] * 1e-3) / 1e9,
                                   "hbm_frac": cb / (m[0] * 1e-3) / 1e9 / PEAK_HBM_GBS}
         del opc, lpc, obc
+        # ---- standalone row softmax (32768 rows x 4096 fp32; and 4096 x 32768) -------------
+        extra["softmax"] = softmax_figures(sa, dev)
 
     value = res.get("prefill_tflops")
     line = {

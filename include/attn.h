@@ -137,6 +137,26 @@ int attn_fwd_splitk_fused(const void* q, const void* k, const void* v, void* out
 int attn_combine(const float* o_partial, const float* lse_partial, void* out, float* lse_out, int P,
                  int rows, int heads, int depth, int out_dtype, void* stream);
 
+/*
+ * attn_softmax_rows -- standalone row softmax, y[r, j] = exp(x[r, j] - m_r) / sum_j' exp(x[r, j'] - m_r)
+ *   with m_r the row maximum, under the all-masked conventions of Tylo.jl "Register fragments and
+ *   logical axes", section "Worked softmax": x = -inf marks a masked entry (y = 0 there), and a row
+ *   whose entries are all -inf gives y = 0 throughout (never NaN).  Other values must be finite.
+ *   x, y      row-major [rows, n] of `dtype` (ATTN_BF16, ATTN_FP16 or ATTN_FP32), aligned to the
+ *             element size; y is rounded to nearest even for 16-bit types.  x == y (in place) is
+ *             allowed; other overlap is not.
+ *   method    ATTN_SOFTMAX_STREAMING: two passes with four values per lane per step, whatever n
+ *               (statistics streamed first, logits reread to write; Tylo "Streaming attention and
+ *               online state", section "Online statistics");
+ *             ATTN_SOFTMAX_REGISTERS: the whole row held in registers, n <= 4096, one read;
+ *             ATTN_SOFTMAX_THREE_PASS: a scalar loop over max, sum of exponentials, write.
+ *             All three compute the same function; they differ in memory traffic and registers.
+ *   Errors: ATTN_E_NULL, ATTN_E_SHAPE (rows or n < 1, sizes overflow), ATTN_E_UNSUPPORTED (dtype,
+ *   method, or n > 4096 with the registers method), ATTN_E_ALIGN.
+ */
+enum attn_softmax_method { ATTN_SOFTMAX_STREAMING = 0, ATTN_SOFTMAX_REGISTERS = 1, ATTN_SOFTMAX_THREE_PASS = 2 };
+int attn_softmax_rows(const void* x, void* y, int64_t rows, int n, int dtype, int method, void* stream);
+
 /* Extended forward call for tests and tuning: every attn_fwd argument plus the key-tile width. */
 struct attn_fwd_args {
   const void* q;

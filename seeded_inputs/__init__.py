@@ -26,6 +26,9 @@ PREFILL = dict(name="causal prefill B4 H32 N4096 D128 bf16", B=4, H=32, N=4096, 
 DECODE = dict(name="split-K decode B8 H32 Nq1 Nkv32768 D128 bf16", B=8, H=32, Nq=1, Nkv=32768, D=128,
               P_list=(4, 8, 16, 37))
 MASKED = dict(name="masked causal B1 H16 N16384 D256 bf16", B=1, H=16, N=16384, D=256, causal=True)
+# standalone row softmax: rows of attention-score logits (a second workload on the same primitives)
+SOFTMAX = dict(name="row softmax 32768 rows x 4096 logits fp32", rows=32768, n=4096, dtype="f32")
+SOFTMAX_WIDE = dict(name="row softmax 4096 rows x 32768 logits fp32", rows=4096, n=32768, dtype="f32")
 
 SWEEP_N = (1, 17, 1000, 2047, 2048)
 SWEEP_D = (16, 32, 64)
@@ -33,7 +36,7 @@ SWEEP_DTYPES = ("bf16", "f16")
 SWEEP_BN = (32, 64)
 SWEEP_VARIANTS = ("normal", "large", "uniform")
 
-CFG_SMALL, CFG_SWEEP, CFG_PREFILL, CFG_DECODE, CFG_MASKED = 1, 2, 3, 4, 5
+CFG_SMALL, CFG_SWEEP, CFG_PREFILL, CFG_DECODE, CFG_MASKED, CFG_SOFTMAX = 1, 2, 3, 4, 5, 6
 
 
 def rng_for(cfg, case):
@@ -143,3 +146,18 @@ def masked_inputs(dtype="bf16", H=None, N=None):
     q, k, v = draw_qkv(rng, (s["B"], N, H, s["D"]), (s["B"], N, H, s["D"]))
     mask, rows = bernoulli_mask(rng, N, N, N // 64)
     return cast(q, dtype), cast(k, dtype), cast(v, dtype), mask, rows
+
+
+def softmax_inputs(rows, n, case=0, variant="normal", masked_frac=0.0, full_rows=0):
+    """float32 [rows, n] logits for the row softmax: standard_normal (x30 for 'large'); then, if
+    masked_frac > 0, each entry is masked (-inf) with that probability (uniform < masked_frac,
+    row-major); then full_rows seeded rows (without replacement) are set to all -inf."""
+    rng = rng_for(CFG_SOFTMAX, case)
+    x = _normal(rng, (rows, n))
+    if variant == "large":
+        x = x * np.float32(30.0)
+    if masked_frac > 0:
+        x[rng.random((rows, n)) < masked_frac] = -np.inf
+    if full_rows:
+        x[rng.choice(rows, size=full_rows, replace=False)] = -np.inf
+    return x

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI in include/attn.h):
     attn_fwd_splitk_fused(q, k, v, P, o_partial, lse_partial, tickets, out, lse=None, causal=False,
                           mask=None, stream=None)
     attn_combine(o_partial, lse_partial, out, lse_out=None, stream=None)
+    attn_softmax_rows(x, y, method=SOFTMAX_STREAMING, stream=None)   (x, y: [..., n])
     attn_last_error(), attn_abi_version()
 Tensors are torch tensors on the GPU, contiguous, laid out as the header states
 (q/out [B, Nq, H, D]; k/v [B, Nkv, H, D]; o_partial [P, B*Nq, H, D]; lse_partial [P, B*Nq, H];
@@ -31,6 +32,7 @@ ATTN_BF16, ATTN_FP16, ATTN_FP32 = 0, 1, 2
 STATUS = {0: "ATTN_OK", 1: "ATTN_E_NULL", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUPPORTED",
           4: "ATTN_E_ALIGN", 5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
 P_MAX = 256
+SOFTMAX_STREAMING, SOFTMAX_REGISTERS, SOFTMAX_THREE_PASS = 0, 1, 2
 
 
 class AttnError(RuntimeError):
@@ -68,6 +70,8 @@ def _load():
     L.attn_fwd_splitk.restype = i32
     L.attn_fwd_splitk_fused.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp, vp, vp, i32, vp]
     L.attn_fwd_splitk_fused.restype = i32
+    L.attn_softmax_rows.argtypes = [vp, vp, ctypes.c_int64, i32, i32, i32, vp]
+    L.attn_softmax_rows.restype = i32
     L.attn_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     L.attn_combine.restype = i32
     L.attn_fwd_ex.argtypes = [ctypes.POINTER(FwdArgs), vp]
@@ -155,6 +159,12 @@ def attn_combine(o_partial, lse_partial, out, lse_out=None, stream=None):
                             rows, heads, depth, _dtype_code(out), _stream(stream)))
 
 
+def attn_softmax_rows(x, y, method=SOFTMAX_STREAMING, stream=None):
+    n = x.shape[-1]
+    rows = x.numel() // n
+    _check(lib().attn_softmax_rows(_ptr(x), _ptr(y), rows, n, _dtype_code(x), int(method), _stream(stream)))
+
+
 # ---- allocating helpers -------------------------------------------------------------------
 def fwd(q, k, v, causal=False, mask=None, block_n=0, with_lse=True):
     out = torch.empty_like(q)
@@ -178,6 +188,12 @@ def splitk(q, k, v, P, causal=False, mask=None, combine=True):
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     attn_fwd_splitk(q, k, v, P, o_p, l_p, out=out, lse=lse, causal=causal, mask=mask)
     return o_p, l_p, out, lse
+
+
+def softmax_rows(x, method=SOFTMAX_STREAMING):
+    y = torch.empty_like(x)
+    attn_softmax_rows(x, y, method)
+    return y
 
 
 def tickets(q):

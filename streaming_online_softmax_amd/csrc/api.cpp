@@ -196,6 +196,24 @@ int attn_fwd_splitk_fused(const void* q, const void* k, const void* v, void* out
   return hip_status(attn::launch_decode(p, dtype, D, true, (hipStream_t)stream), "attn_fwd_splitk_fused launch");
 }
 
+int attn_softmax_rows(const void* x, void* y, int64_t rows, int n, int dtype, int method, void* stream) {
+  if (!x || !y) return fail(ATTN_E_NULL, "x and y must be non-NULL device pointers");
+  if (rows < 1 || n < 1) return fail(ATTN_E_SHAPE, "rows and n must be >= 1 (got %lld, %d)", (long long)rows, n);
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16 && dtype != ATTN_FP32) return fail(ATTN_E_UNSUPPORTED, "dtype %d not supported", dtype);
+  if (method != ATTN_SOFTMAX_STREAMING && method != ATTN_SOFTMAX_REGISTERS && method != ATTN_SOFTMAX_THREE_PASS)
+    return fail(ATTN_E_UNSUPPORTED, "softmax method %d not supported", method);
+  if (method == ATTN_SOFTMAX_REGISTERS && n > attn::softmax_regs_max_n())
+    return fail(ATTN_E_UNSUPPORTED, "the registers method holds rows of at most %d elements (got %d)", attn::softmax_regs_max_n(), n);
+  if ((rows + 3) / 4 > 0x7fffffffLL || (double)rows * n > 4.0e18) return fail(ATTN_E_SHAPE, "rows * n too large");
+  const uintptr_t es = dtype == ATTN_FP32 ? 4 : 2;
+  if (!aligned(x, es) || !aligned(y, es)) return fail(ATTN_E_ALIGN, "x and y must be aligned to their element size");
+  const uintptr_t vb = 4 * es;   // four elements per vector access
+  const bool vec = (n % 4 == 0) && aligned(x, vb) && aligned(y, vb);
+  attn::SoftmaxParams p{x, y, rows, n};
+  const int dt = dtype == ATTN_BF16 ? 0 : (dtype == ATTN_FP16 ? 1 : 2);
+  return hip_status(attn::launch_softmax_rows(p, dt, method, vec, (hipStream_t)stream), "attn_softmax_rows launch");
+}
+
 int attn_combine(const float* o_partial, const float* lse_partial, void* out, float* lse_out, int P,
                  int rows, int heads, int depth, int out_dtype, void* stream) {
   int rc = check_combine(o_partial, lse_partial, out, lse_out, P, rows, heads, depth, out_dtype);

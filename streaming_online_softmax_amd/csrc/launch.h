@@ -56,7 +56,18 @@ struct CombineParams {
   int RH;               // rows * heads
 };
 
+// Standalone row softmax (attn_softmax_rows).
+enum { SM_STREAM = 0, SM_REGS = 1, SM_THREE = 2 };
+struct SoftmaxParams {
+  const void* x;        // [rows, n] logits
+  void* y;              // [rows, n] probabilities, same element type
+  int64_t rows;
+  int n;
+};
+
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int BN, bool split, hipStream_t s);
+hipError_t launch_softmax_rows(const SoftmaxParams& p, int dtype, int method, bool vec, hipStream_t s);
+int softmax_regs_max_n();
 hipError_t launch_decode(const DecodeParams& p, int dtype, int D, bool fused, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, int depth, int out_dtype, hipStream_t s);
 int fwd_block_m();

@@ -13,8 +13,8 @@ E_NULL, E_SHAPE, E_UNSUP, E_ALIGN, E_WS = 1, 2, 3, 4, 5
 
 def test_library_exports_every_declared_symbol():
     names = sa.declared_symbols()
-    assert {"attn_fwd", "attn_fwd_splitk", "attn_fwd_splitk_fused", "attn_combine", "attn_fwd_ex",
-            "attn_last_error", "attn_abi_version"} <= set(names)
+    assert {"attn_fwd", "attn_fwd_splitk", "attn_fwd_splitk_fused", "attn_combine", "attn_softmax_rows",
+            "attn_fwd_ex", "attn_last_error", "attn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(sa.lib(), n), n
 
@@ -43,6 +43,10 @@ def fused(q=A, k=A, v=A, out=A, lse=None, B=1, H=1, Nq=1, Nkv=64, D=64, causal=0
           o_p=A, l_p=A, tk=A, dtype=0):
     return sa.lib().attn_fwd_splitk_fused(q, k, v, out, lse, B, H, Nq, Nkv, D, causal, mask, P, o_p, l_p, tk,
                                           dtype, None)
+
+
+def softmax(x=A, y=A, rows=1, n=64, dtype=2, method=0):
+    return sa.lib().attn_softmax_rows(x, y, rows, n, dtype, method, None)
 
 
 def combine(o_p=A, l_p=A, out=A, lse=None, P=4, rows=1, heads=1, depth=64, out_dtype=2):
@@ -74,6 +78,13 @@ def combine(o_p=A, l_p=A, out=A, lse=None, P=4, rows=1, heads=1, depth=64, out_d
     (lambda: fused(tk=A + 2), E_ALIGN),
     (lambda: fused(P=300), E_UNSUP),
     (lambda: fused(causal=1), E_SHAPE),
+    (lambda: softmax(x=None), E_NULL),
+    (lambda: softmax(rows=0), E_SHAPE),
+    (lambda: softmax(n=0), E_SHAPE),
+    (lambda: softmax(dtype=5), E_UNSUP),
+    (lambda: softmax(method=3), E_UNSUP),
+    (lambda: softmax(method=1, n=4097), E_UNSUP),
+    (lambda: softmax(x=A + 2), E_ALIGN),
     (lambda: combine(P=0), E_SHAPE),
     (lambda: combine(P=300), E_UNSUP),
     (lambda: combine(depth=100), E_UNSUP),
