@@ -285,7 +285,7 @@ def main():
         line["roofline"] = {"bound": "mfma", "achieved": value, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                             "frac": value / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
                             "traffic_unit": "bytes per launch (HBM, counter-measured)",
-                            "kernel": "attn_fwd_kernel<bf16, D=128, BN=64>",
+                            "kernel": "attn_fwd_kernel<bf16, D=128, BN=64, waves=8, stages=3>",
                             "work_per_launch": f"{fl:.4e} FLOP (4*D per causal pair)"}
     line.update(extra)
     if args.only is None and not args.no_cpu_baseline:
