@@ -1,7 +1,7 @@
 /*
  * attn.h -- C ABI of libattn.so: streaming (online-softmax) attention for AMD MI355X (gfx950).
  *
- * Three operations, each a hand-written HIP kernel enqueued on the caller's stream:
+ * Operations, each a hand-written HIP kernel enqueued on the caller's stream:
  *
  *   attn_fwd         out = softmax(Q K^T / sqrt(D)) V over visible keys, computed tile by tile
  *                    with the online-softmax recurrence (running max m, FP32 denominator l, FP32
@@ -15,6 +15,11 @@
  *                    workspace.  Source: Modular MAX "fa4_splitk_combine", workspace layout.
  *   attn_combine     the LSE-weighted merge of such a workspace.  Source: Modular MAX
  *                    "fa4_splitk_combine", per-row-head formulas (base 2 throughout).
+ *   attn_fwd_splitk_fused   attn_fwd_splitk and attn_combine in one launch (the last
+ *                    workgroup of each row-head merges).
+ *   attn_softmax_rows        standalone row softmax (streaming, registers or three-pass)
+ *                    with the all-masked conventions of Tylo.jl "Register fragments and
+ *                    logical axes", section "Worked softmax".
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library allocates
@@ -27,7 +32,7 @@
  *     this boundary.
  *   - Layouts are contiguous, D fastest: q and out are [B, Nq, H, D]; k and v are [B, Nkv, H, D].
  *     A row-head is one query row of one head, rh = (b * Nq + i) * H + h.
- *   - q, k, v share one element type (ATTN_BF16 or ATTN_FP16); `out` of attn_fwd uses it too,
+ *   - Attention entry points: q, k, v share one element type (ATTN_BF16 or ATTN_FP16); `out` uses it too,
  *     rounded to nearest even.  Scores, the softmax state, accumulation and every LSE are FP32.
  *     The weights p are rounded to the input type (nearest even) before the P.V product while
  *     the denominator sums the unrounded FP32 p (Tylo "Attention as a consumer").
