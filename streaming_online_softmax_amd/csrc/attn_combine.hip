@@ -1,14 +1,16 @@
 // attn_combine.hip -- LSE-weighted merge of a split-K workspace (Modular MAX
 // "fa4_splitk_combine": per-row-head formulas, base 2 throughout, and its performance
 // structure), written for wave64:
-//   * one wave per output row-head; the row's depth is split into 16-byte lane slices, and
-//     64 / (depth/4) partitions are folded concurrently by separate lane groups;
+//   * one wave per output row-head, four row-heads per workgroup (fewer, larger workgroups to
+//     dispatch); the row's depth is split into 16-byte lane slices, and 64 / (depth/4)
+//     partitions are folded concurrently by separate lane groups;
 //   * the LSE reduction (max, log-sum-exp, per-partition scale) is computed once into lane
 //     registers: lane t holds partitions t, t+64, ...;
 //   * each partition's scale reaches its lane group by a cross-lane read (ds_bpermute) for the
 //     unrolled small-P instantiations, or from a 256-entry LDS table for the runtime-P one;
-//   * the next partition's slice is loaded before the current one is folded (software
-//     pipelining), so load latency overlaps the FMAs.
+//   * loads run ahead of the FMAs: for the unrolled P every slice of the row-head is loaded
+//     before the first is folded; for the runtime P the next slices are loaded before the
+//     current ones are folded (software pipelining), so load latency overlaps the FMAs.
 // An empty partition (lse = -inf) gets scale exactly 0; if every partition is empty the output
 // is 0 and the LSE -inf (the all-masked convention of Tylo.jl "Register fragments and logical
 // axes", section "Worked softmax", applied to the merge).
@@ -34,18 +36,30 @@ template <> struct out_store<f16_t> {
   }
 };
 
+constexpr int kCombineWaves = 4;   // row-heads (waves) per workgroup
+
+// The workspace is read exactly once: non-temporal (streaming) loads keep it from displacing
+// other lines in the caches.
+__device__ __forceinline__ f32x4 ld_stream(const float* a) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a));
+}
+
 template <int P_STATIC, int DEPTH, typename TO>
-__global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
+__global__ __launch_bounds__(64 * kCombineWaves) void attn_combine_kernel(CombineParams p) {
   constexpr int LPP = DEPTH / 4;              // lanes per partition slice (16 bytes each)
   constexpr int G = 64 / LPP;                 // partitions folded at once
   constexpr int NL = P_STATIC ? (P_STATIC + 63) / 64 : ATTN_P_MAX_DEV / 64;
   const int P = P_STATIC ? P_STATIC : p.P;
 
-  __shared__ float sc_lds[P_STATIC ? 1 : ATTN_P_MAX_DEV];
+  __shared__ float sc_lds[P_STATIC ? 1 : kCombineWaves][P_STATIC ? 1 : ATTN_P_MAX_DEV];
 
-  const int lane = threadIdx.x;
-  const int64_t rh = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t RH = p.RH;
+  // a wave past the last row-head computes on row-head RH-1 and stores nothing (it still
+  // reaches the workgroup barrier of the runtime-P path)
+  const int64_t rh_w = (int64_t)blockIdx.x * kCombineWaves + wave;
+  const bool live = rh_w < RH;
+  const int64_t rh = live ? rh_w : RH - 1;
 
   // ---- LSE phase: once per row-head, into registers
   float ls[NL];
@@ -69,8 +83,8 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
   for (int t = 0; t < NL; ++t) sc[t] = (empty || ls[t] == kNegInf) ? 0.f : fast_exp2(ls[t] - Gl);
   if constexpr (!P_STATIC) {
 #pragma unroll
-    for (int t = 0; t < NL; ++t) sc_lds[lane + 64 * t] = sc[t];
-    __syncthreads();   // one-wave workgroup: orders the table writes before the reads
+    for (int t = 0; t < NL; ++t) sc_lds[wave][lane + 64 * t] = sc[t];
+    __syncthreads();   // orders each wave's table writes before its reads
   }
 
   // ---- weighted accumulation over partitions, next slice prefetched
@@ -82,24 +96,28 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
       // pp < P_STATIC <= 64: partition pp lives in lane pp, register 0
       return __shfl(sc[0], pp < P ? pp : 0, 64) * (pp < P ? 1.f : 0.f);
     } else {
-      return pp < P ? sc_lds[pp] : 0.f;
+      return pp < P ? sc_lds[wave][pp] : 0.f;
     }
   };
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 cur = g < P ? *reinterpret_cast<const f32x4*>(src + (int64_t)g * pstride) : f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (P_STATIC) {
+    constexpr int NS = (P_STATIC + G - 1) / G;   // slices per lane group
+    f32x4 slice[NS];
 #pragma unroll
-    for (int pp0 = 0; pp0 < P_STATIC; pp0 += G) {
-      const int pn = pp0 + G + g;
-      f32x4 nxt = pn < P ? *reinterpret_cast<const f32x4*>(src + (int64_t)pn * pstride) : f32x4{0.f, 0.f, 0.f, 0.f};
-      const float s = scale_of(pp0 + g);
-      acc += (s != 0.f) ? s * cur : f32x4{0.f, 0.f, 0.f, 0.f};   // an empty partition adds nothing
-      cur = nxt;
+    for (int i = 0; i < NS; ++i) {
+      const int pp = i * G + g;
+      slice[i] = pp < P ? ld_stream(src + (int64_t)pp * pstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const float s = scale_of(i * G + g);
+      acc += (s != 0.f) ? s * slice[i] : f32x4{0.f, 0.f, 0.f, 0.f};   // an empty partition adds nothing
     }
   } else {
+    f32x4 cur = g < P ? ld_stream(src + (int64_t)g * pstride) : f32x4{0.f, 0.f, 0.f, 0.f};
     for (int pp0 = 0; pp0 < P; pp0 += G) {
       const int pn = pp0 + G + g;
-      f32x4 nxt = pn < P ? *reinterpret_cast<const f32x4*>(src + (int64_t)pn * pstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 nxt = pn < P ? ld_stream(src + (int64_t)pn * pstride) : f32x4{0.f, 0.f, 0.f, 0.f};
       const float s = scale_of(pp0 + g);
       acc += (s != 0.f) ? s * cur : f32x4{0.f, 0.f, 0.f, 0.f};   // an empty partition adds nothing
       cur = nxt;
@@ -107,16 +125,17 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = across_groups_sum<LPP>(acc[j]);
-  if (g == 0) out_store<TO>::put4(p.out, rh * DEPTH + dl * 4, acc);
-  if (lane == 0 && p.lse_out) p.lse_out[rh] = empty ? kNegInf : Gl * kLn2;
+  if (live && g == 0) out_store<TO>::put4(p.out, rh * DEPTH + dl * 4, acc);
+  if (live && lane == 0 && p.lse_out) p.lse_out[rh] = empty ? kNegInf : Gl * kLn2;
 }
 
 template <int P_STATIC, int DEPTH>
 static hipError_t launch_combine_t(const CombineParams& p, int out_dtype, hipStream_t s) {
-  dim3 grid((unsigned)p.RH);
-  if (out_dtype == 2) hipLaunchKernelGGL((attn_combine_kernel<P_STATIC, DEPTH, float>), grid, dim3(64), 0, s, p);
-  else if (out_dtype == 0) hipLaunchKernelGGL((attn_combine_kernel<P_STATIC, DEPTH, bf16_t>), grid, dim3(64), 0, s, p);
-  else hipLaunchKernelGGL((attn_combine_kernel<P_STATIC, DEPTH, f16_t>), grid, dim3(64), 0, s, p);
+  dim3 grid((unsigned)((p.RH + kCombineWaves - 1) / kCombineWaves));
+  dim3 block(64 * kCombineWaves);
+  if (out_dtype == 2) hipLaunchKernelGGL((attn_combine_kernel<P_STATIC, DEPTH, float>), grid, block, 0, s, p);
+  else if (out_dtype == 0) hipLaunchKernelGGL((attn_combine_kernel<P_STATIC, DEPTH, bf16_t>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((attn_combine_kernel<P_STATIC, DEPTH, f16_t>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
