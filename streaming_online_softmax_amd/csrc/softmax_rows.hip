@@ -19,22 +19,29 @@
 
 namespace attn {
 
-// element access: 4 consecutive elements as floats, and the rounding store back
+// element access: 4 consecutive elements as floats, and the rounding store back.  The
+// probabilities are written once and never reread here, so they are stored non-temporally; a
+// load marked LAST is the final read of those logits (it need not stay in the caches).
+template <typename T> __device__ __forceinline__ T ld_nt_if(const T* a, bool nt) {
+  return nt ? __builtin_nontemporal_load(a) : *a;
+}
 template <typename TE> struct sm_io;
 template <> struct sm_io<float> {
+  template <bool LAST = false>
   static __device__ __forceinline__ f32x4 load4(const void* base, int64_t i) {
-    return *reinterpret_cast<const f32x4*>((const float*)base + i);
+    return ld_nt_if(reinterpret_cast<const f32x4*>((const float*)base + i), LAST);
   }
   static __device__ __forceinline__ float load1(const void* base, int64_t i) { return ((const float*)base)[i]; }
   static __device__ __forceinline__ void store4(void* base, int64_t i, f32x4 v) {
-    *reinterpret_cast<f32x4*>((float*)base + i) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>((float*)base + i));
   }
   static __device__ __forceinline__ void store1(void* base, int64_t i, float v) { ((float*)base)[i] = v; }
 };
 template <typename T16> struct sm_io16 {
   using E = elem<T16>;
+  template <bool LAST = false>
   static __device__ __forceinline__ f32x4 load4(const void* base, int64_t i) {
-    const u32x2 w = *reinterpret_cast<const u32x2*>((const uint16_t*)base + i);
+    const u32x2 w = ld_nt_if(reinterpret_cast<const u32x2*>((const uint16_t*)base + i), LAST);
     return f32x4{E::to_f32((uint16_t)(w[0] & 0xFFFFu)), E::to_f32((uint16_t)(w[0] >> 16)),
                  E::to_f32((uint16_t)(w[1] & 0xFFFFu)), E::to_f32((uint16_t)(w[1] >> 16))};
   }
@@ -42,7 +49,7 @@ template <typename T16> struct sm_io16 {
     return E::to_f32(((const uint16_t*)base)[i]);
   }
   static __device__ __forceinline__ void store4(void* base, int64_t i, f32x4 v) {
-    *reinterpret_cast<u32x2*>((uint16_t*)base + i) = u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+    __builtin_nontemporal_store(u32x2{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])}, reinterpret_cast<u32x2*>((uint16_t*)base + i));
   }
   static __device__ __forceinline__ void store1(void* base, int64_t i, float v) {
     ((uint16_t*)base)[i] = (uint16_t)(E::pack2(v, 0.f) & 0xFFFFu);
@@ -113,7 +120,7 @@ __global__ __launch_bounds__(256) void softmax_rows_kernel(SoftmaxParams p) {
     for (; j + 256 * (U - 1) < nv; j += 256 * U) {
       f32x4 v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = IO::load4(p.x, base + j + 256 * u);
+      for (int u = 0; u < U; ++u) v[u] = IO::template load4<true>(p.x, base + j + 256 * u);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         f32x4 y;
@@ -123,7 +130,7 @@ __global__ __launch_bounds__(256) void softmax_rows_kernel(SoftmaxParams p) {
       }
     }
     for (; j < nv; j += 256) {
-      const f32x4 v = IO::load4(p.x, base + j);
+      const f32x4 v = IO::template load4<true>(p.x, base + j);
       f32x4 y;
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[e] = sm_weight(v[e], mref) * inv;
@@ -137,7 +144,7 @@ __global__ __launch_bounds__(256) void softmax_rows_kernel(SoftmaxParams p) {
     for (int r = 0; r < R; ++r) {
       const int j = 256 * r + 4 * lane;
       if (VEC && j + 3 < n) {
-        v[r] = IO::load4(p.x, base + j);
+        v[r] = IO::template load4<true>(p.x, base + j);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[r][e] = (j + e < n) ? IO::load1(p.x, base + j + e) : kNegInf;
