@@ -293,6 +293,23 @@ def test_decode_fused_empty_and_masked(sa):
     assert bool((out[0, 1] == 0).all()) and bool(torch.isneginf(lse[0, 1]).all())
 
 
+@pytest.mark.parametrize("P,D", [(1, 64), (200, 128), (256, 16)])
+def test_decode_fused_partition_extremes(sa, P, D):
+    """Fused decode at one partition (the merge is the identity) and at up to 256 partitions
+    (one per thread of the merging workgroup), with causal square shapes (Nq = Nkv = 3) too."""
+    rng = si.rng_for(92, P)
+    q, k, v = (si.cast(x, "bf16") for x in si.draw_qkv(rng, (2, 1, 4, D), (2, 3000, 4, D)))
+    out, lse, _, _ = sa.splitk_fused(q.to(DEV), k.to(DEV), v.to(DEV), P)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.attn_dense(q, k, v)
+    _compare(out.reshape(8, -1), lse.reshape(-1), ref, ref_lse, "bf16", f"fused P={P} D={D}")
+    q, k, v = (si.cast(x, "f16") for x in si.draw_qkv(rng, (1, 3, 2, D), (1, 3, 2, D)))
+    out, lse, _, _ = sa.splitk_fused(q.to(DEV), k.to(DEV), v.to(DEV), min(P, 5), causal=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.attn_dense(q, k, v, causal=True)
+    _compare(out.reshape(6, -1), lse.reshape(-1), ref, ref_lse, "f16", f"fused causal P={min(P, 5)}")
+
+
 @pytest.mark.parametrize("P", [1, 3, 7])
 def test_square_causal_split_matches_unsplit(sa, P):
     """Square causal shapes through the matrix-core split path.  Here |O| reaches ~3 and the
