@@ -10,8 +10,9 @@ One step is one pass over every kernel of the path, on resident synthetic inputs
 query-key pair, causal diagonal included); the decode and combine bandwidths are reported
 beside it, together with a decode sweep over P in {4, 8, 16, 37} (two launches, and the same
 work fused into one attn_fwd_splitk_fused launch) and a combine measured on a workspace too large
-for the caches, and the standalone row softmax (three methods) on 32768 x 4096 and 4096 x 32768
-fp32 rows.  Every per-kernel time comes from HIP events recorded on the
+for the caches, the standalone row softmax (three methods) on 32768 x 4096 and 4096 x 32768
+fp32 rows, and the masked long-context prefill (B1 H16 N16384 D256, causal AND a Bernoulli(0.5)
+mask with 1/64 of the rows fully masked) beside the same shape without the mask.  Every per-kernel time comes from HIP events recorded on the
 stream the kernels are launched on, over the whole timed region.  Rank 0 prints one JSON line.
 """
 import argparse
@@ -63,6 +64,31 @@ def softmax_figures(sa, dev, steps=10, warmup=3):
         res[w["name"]] = fig
         del x, y
     return res
+
+
+def masked_figures(sa, dev, steps=10, warmup=3):
+    """attn_fwd on the masked long-context workload, and on the same tensors without the mask.
+    TFLOP/s counts 4*D per causal pair (the work the kernel does); 'useful' counts only the pairs
+    the mask leaves visible."""
+    s = si.MASKED
+    qc, kc, vc, mask, _ = si.masked_inputs()
+    vis = 0
+    for r0 in range(0, s["N"], 2048):                  # visible pairs of causal AND mask, in row blocks
+        blk = mask[r0:r0 + 2048]
+        vis += int(np.count_nonzero(np.tril(blk, k=r0)))
+    q, k, v = qc.to(dev), kc.to(dev), vc.to(dev)
+    md = torch.from_numpy(mask).to(dev)
+    del qc, kc, vc, mask
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    fl = prefill_flops(s["B"], s["H"], s["N"], s["D"])
+    useful = 4.0 * s["D"] * vis * s["B"] * s["H"]
+    _, m = timed_events([lambda: sa.attn_fwd(q, k, v, out, lse, causal=True, mask=md),
+                         lambda: sa.attn_fwd(q, k, v, out, lse, causal=True)], steps, warmup)
+    return {"B": s["B"], "H": s["H"], "N": s["N"], "D": s["D"], "masked_ms": m[0],
+            "masked_TFLOP/s": fl / (m[0] * 1e-3) / 1e12, "mfma_frac": fl / (m[0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "useful_TFLOP/s": useful / (m[0] * 1e-3) / 1e12, "visible_pair_frac": vis / (s["N"] * (s["N"] + 1) / 2),
+            "causal_only_ms": m[1], "causal_only_TFLOP/s": fl / (m[1] * 1e-3) / 1e12}
 
 
 def combine_bytes(P, RH, D, out_elem=2):
@@ -255,6 +281,8 @@ def main():
         del opc, lpc, obc
         # ---- standalone row softmax (32768 rows x 4096 fp32; and 4096 x 32768) -------------
         extra["softmax"] = softmax_figures(sa, dev)
+        # ---- masked long context B1 H16 N16384 D256, causal AND Bernoulli(0.5) mask ----------
+        extra["masked_long_context"] = masked_figures(sa, dev)
 
     value = res.get("prefill_tflops")
     line = {

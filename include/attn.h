@@ -20,6 +20,8 @@
  *   attn_softmax_rows        standalone row softmax (streaming, registers or three-pass)
  *                    with the all-masked conventions of Tylo.jl "Register fragments and
  *                    logical axes", section "Worked softmax".
+ *   attn_round       FP32 -> bf16 / fp16 with the conversion the kernels apply to the
+ *                    probabilities and to the output (exposed so it can be checked bit by bit).
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library allocates
@@ -161,6 +163,20 @@ int attn_combine(const float* o_partial, const float* lse_partial, void* out, fl
  */
 enum attn_softmax_method { ATTN_SOFTMAX_STREAMING = 0, ATTN_SOFTMAX_REGISTERS = 1, ATTN_SOFTMAX_THREE_PASS = 2 };
 int attn_softmax_rows(const void* x, void* y, int64_t rows, int n, int dtype, int method, void* stream);
+
+/*
+ * attn_round -- y[i] = x[i] rounded to bf16 or fp16, to nearest with ties to even, by the packed
+ *   conversion the attention kernels use for the probabilities before the second product and for
+ *   the stored output (Tylo.jl "Streaming attention and online state", section "Same-lane
+ *   conversion": round to nearest even, signed zeros and infinities kept, NaN stays NaN, no
+ *   saturation and no flush to zero; Tylo.jl "Register fragments and logical axes", section
+ *   "Logical types and register packing": the packed word).  Values beyond the largest finite value become +-inf; +-0 and +-inf keep their
+ *   sign; NaN gives a NaN.
+ *   x      n FP32 values (device, 4-byte aligned);  y  n 16-bit results (device, 2-byte aligned).
+ *   dtype  ATTN_BF16 or ATTN_FP16.  n = 0 enqueues nothing.
+ *   Errors: ATTN_E_SHAPE (n < 0), ATTN_E_NULL, ATTN_E_UNSUPPORTED (dtype), ATTN_E_ALIGN.
+ */
+int attn_round(const float* x, void* y, int64_t n, int dtype, void* stream);
 
 /* Extended forward call for tests and tuning: every attn_fwd argument plus the key-tile width. */
 struct attn_fwd_args {

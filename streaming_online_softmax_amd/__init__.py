@@ -12,6 +12,7 @@ Entry points (same names as the C ABI in include/attn.h):
                           mask=None, stream=None)
     attn_combine(o_partial, lse_partial, out, lse_out=None, stream=None)
     attn_softmax_rows(x, y, method=SOFTMAX_STREAMING, stream=None)   (x, y: [..., n])
+    attn_round(x, y, stream=None)    (x float32, y bf16/fp16, same number of elements)
     attn_last_error(), attn_abi_version()
 Tensors are torch tensors on the GPU, contiguous, laid out as the header states
 (q/out [B, Nq, H, D]; k/v [B, Nkv, H, D]; o_partial [P, B*Nq, H, D]; lse_partial [P, B*Nq, H];
@@ -72,6 +73,8 @@ def _load():
     L.attn_fwd_splitk_fused.restype = i32
     L.attn_softmax_rows.argtypes = [vp, vp, ctypes.c_int64, i32, i32, i32, vp]
     L.attn_softmax_rows.restype = i32
+    L.attn_round.argtypes = [vp, vp, ctypes.c_int64, i32, vp]
+    L.attn_round.restype = i32
     L.attn_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     L.attn_combine.restype = i32
     L.attn_fwd_ex.argtypes = [ctypes.POINTER(FwdArgs), vp]
@@ -163,6 +166,13 @@ def attn_softmax_rows(x, y, method=SOFTMAX_STREAMING, stream=None):
     n = x.shape[-1]
     rows = x.numel() // n
     _check(lib().attn_softmax_rows(_ptr(x), _ptr(y), rows, n, _dtype_code(x), int(method), _stream(stream)))
+
+
+def attn_round(x, y, stream=None):
+    """y (bf16 or fp16) = x (fp32) rounded to nearest even by the kernels' packed conversion."""
+    if x.dtype != torch.float32 or x.numel() != y.numel():
+        raise AttnError(2, "x must be float32 with as many elements as y")
+    _check(lib().attn_round(_ptr(x), _ptr(y), x.numel(), _dtype_code(y), _stream(stream)))
 
 
 # ---- allocating helpers -------------------------------------------------------------------

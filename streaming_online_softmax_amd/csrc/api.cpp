@@ -214,6 +214,15 @@ int attn_softmax_rows(const void* x, void* y, int64_t rows, int n, int dtype, in
   return hip_status(attn::launch_softmax_rows(p, dt, method, vec, (hipStream_t)stream), "attn_softmax_rows launch");
 }
 
+int attn_round(const float* x, void* y, int64_t n, int dtype, void* stream) {
+  if (n < 0) return fail(ATTN_E_SHAPE, "n must be >= 0 (got %lld)", (long long)n);
+  if (n == 0) return ATTN_OK;
+  if (!x || !y) return fail(ATTN_E_NULL, "x and y must be non-NULL device pointers");
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return fail(ATTN_E_UNSUPPORTED, "dtype %d not supported (bf16 or fp16)", dtype);
+  if (!aligned(x, 4) || !aligned(y, 2)) return fail(ATTN_E_ALIGN, "x must be 4-byte and y 2-byte aligned");
+  return hip_status(attn::launch_round(x, y, n, dtype == ATTN_BF16 ? 0 : 1, (hipStream_t)stream), "attn_round launch");
+}
+
 int attn_combine(const float* o_partial, const float* lse_partial, void* out, float* lse_out, int P,
                  int rows, int heads, int depth, int out_dtype, void* stream) {
   int rc = check_combine(o_partial, lse_partial, out, lse_out, P, rows, heads, depth, out_dtype);

@@ -68,6 +68,8 @@ struct SoftmaxParams {
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int BN, bool split, hipStream_t s);
 hipError_t launch_softmax_rows(const SoftmaxParams& p, int dtype, int method, bool vec, hipStream_t s);
 int softmax_regs_max_n();
+// FP32 -> bf16 (dtype 0) or fp16 (dtype 1), n values, with the kernels' packed conversion.
+hipError_t launch_round(const float* x, void* y, int64_t n, int dtype, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int dtype, int D, bool fused, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, int depth, int out_dtype, hipStream_t s);
 int fwd_block_m();

@@ -14,7 +14,7 @@ E_NULL, E_SHAPE, E_UNSUP, E_ALIGN, E_WS = 1, 2, 3, 4, 5
 def test_library_exports_every_declared_symbol():
     names = sa.declared_symbols()
     assert {"attn_fwd", "attn_fwd_splitk", "attn_fwd_splitk_fused", "attn_combine", "attn_softmax_rows",
-            "attn_fwd_ex", "attn_last_error", "attn_abi_version"} <= set(names)
+            "attn_round", "attn_fwd_ex", "attn_last_error", "attn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(sa.lib(), n), n
 
@@ -47,6 +47,10 @@ def fused(q=A, k=A, v=A, out=A, lse=None, B=1, H=1, Nq=1, Nkv=64, D=64, causal=0
 
 def softmax(x=A, y=A, rows=1, n=64, dtype=2, method=0):
     return sa.lib().attn_softmax_rows(x, y, rows, n, dtype, method, None)
+
+
+def rnd(x=A, y=A, n=64, dtype=0):
+    return sa.lib().attn_round(x, y, n, dtype, None)
 
 
 def combine(o_p=A, l_p=A, out=A, lse=None, P=4, rows=1, heads=1, depth=64, out_dtype=2):
@@ -85,6 +89,12 @@ def combine(o_p=A, l_p=A, out=A, lse=None, P=4, rows=1, heads=1, depth=64, out_d
     (lambda: softmax(method=3), E_UNSUP),
     (lambda: softmax(method=1, n=4097), E_UNSUP),
     (lambda: softmax(x=A + 2), E_ALIGN),
+    (lambda: rnd(n=-1), E_SHAPE),
+    (lambda: rnd(x=None), E_NULL),
+    (lambda: rnd(y=None), E_NULL),
+    (lambda: rnd(dtype=2), E_UNSUP),
+    (lambda: rnd(x=A + 2), E_ALIGN),
+    (lambda: rnd(y=A + 1), E_ALIGN),
     (lambda: combine(P=0), E_SHAPE),
     (lambda: combine(P=300), E_UNSUP),
     (lambda: combine(depth=100), E_UNSUP),
@@ -100,6 +110,10 @@ def test_reject_paths(call, code):
 
 
 @needs_no_gpu
+def test_round_of_nothing_enqueues_nothing():
+    assert rnd(x=None, y=None, n=0) == 0
+
+
 def test_fwd_ex_rejects_bad_block_n():
     a = sa.FwdArgs(A, A, A, A, None, None, 1, 1, 64, 128, 0, 0, 32)
     assert sa.lib().attn_fwd_ex(ctypes.byref(a), None) == E_UNSUP
