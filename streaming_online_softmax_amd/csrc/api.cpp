@@ -107,6 +107,7 @@ int fwd_impl(const attn_fwd_args* a, hipStream_t s) {
   p.P = 1; p.chunk = a->N;
   p.n_qblocks = (int)nqb;
   p.mask_vec = a->mask && aligned(a->mask, 8) && (a->N % 8 == 0);
+  p.mask_lds = a->mask && aligned(a->mask, 16) && (a->N % 16 == 0) && ((int64_t)a->N + 256) * a->N < (1LL << 32);
   p.scale_log2 = scale_log2(a->D);
   return hip_status(attn::launch_fwd(p, a->dtype, a->D, BN, false, s), "attn_fwd launch");
 }
@@ -165,6 +166,7 @@ int attn_fwd_splitk(const void* q, const void* k, const void* v, void* out, floa
     p.B = B; p.H = H; p.Nq = Nq; p.Nkv = Nkv; p.causal = causal; p.P = P; p.chunk = chunk;
     p.n_qblocks = (int)nqb;
     p.mask_vec = mask && aligned(mask, 8) && (Nkv % 8 == 0) && (chunk % 8 == 0);
+    p.mask_lds = mask && aligned(mask, 16) && (Nkv % 16 == 0) && (chunk % 16 == 0) && ((int64_t)Nq + 256) * Nkv < (1LL << 32);
     p.scale_log2 = c;
     rc = hip_status(attn::launch_fwd(p, dtype, D, 64, true, s), "attn_fwd_splitk launch");
   }

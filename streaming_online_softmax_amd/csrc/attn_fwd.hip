@@ -25,7 +25,9 @@
 //
 // Masking uses selects, never branches around the exponential (Tylo "Attention as a consumer"):
 // the key tail and causal selects run only on tiles that need them, the byte mask on every
-// tile when present.  Wholly future causal tiles are skipped (they would leave the state
+// tile when present; the byte mask's tile (the block's rows x the tile's keys) is staged into
+// LDS with the K and V tiles when its rows are 16-byte aligned, and read from global memory
+// otherwise.  Wholly future causal tiles are skipped (they would leave the state
 // unchanged: workshop "Masks that preserve the recurrence").
 #include "device.h"
 #include "launch.h"
@@ -78,6 +80,16 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   constexpr int KSTEPS = D / 16;        // k-steps of S^T = K Q^T
   constexpr int MT = BN / 32;           // 32-key blocks per tile
   constexpr int DT = DP / 32;           // 32-row tiles of O^T
+  // Mask tiles (MASK): the block's kBlockM query rows x BN key bytes, staged through LDS like K
+  // and V.  Row r's 16-byte chunk c sits at position c ^ msw(r) of the row, so the 32 rows one
+  // wave reads with a single instruction spread over the banks.
+  constexpr int MTILE = MASK ? kBlockM * BN : 0;
+  constexpr int M_CPR = BN / 16;                  // 16-byte chunks per mask row
+  constexpr int M_RPI = 64 / M_CPR;               // mask rows per wave-instruction
+  constexpr int M_RPL = 256 / BN;                 // mask rows per 256-byte bank line
+  constexpr int MPW = MASK ? MTILE / (1024 * WAVES) : 0;   // mask wave-instructions per wave per tile
+  static_assert(!MASK || MTILE % (1024 * WAVES) == 0, "whole mask wave-instructions per wave");
+  static_assert((WAVES * M_RPI / M_RPL) % M_CPR == 0, "mask swizzle independent of the instruction");
   static_assert(WAVES == 4 || WAVES == 8, "four or eight waves per workgroup");
   static_assert(TILE % 1024 == 0, "tile must be a whole number of 1 KiB wave loads");
   // LDS stages: tiles are loaded NSTAGE-1 ahead.  Three stages where one workgroup owns the CU
@@ -90,7 +102,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   static_assert((NSTAGE - 1) * TILE + (MT - 1) * 32 * RB < 65536, "K read offsets exceed the DS immediate");
   static_assert((NSTAGE - 1) * TILE + (BN - 1) * RB < 65536, "V read offsets exceed the DS immediate");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NSTAGE * TILE];
+  constexpr int M_OFS = 2 * NSTAGE * TILE;
+  static_assert(M_OFS + NSTAGE * MTILE <= 160 * 1024, "LDS budget of one workgroup");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[M_OFS + NSTAGE * MTILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -158,6 +172,15 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   constexpr int kTileLoads = 2 * PER_WAVE;
   static_assert(NSTAGE == 2 || NT % WAVES == 0, "three stages need the same load count in every wave");
   constexpr int kWaitAllButOneTile = (kTileLoads & 15) | ((kTileLoads >> 4) << 14) | (7 << 4) | (15 << 8);
+  constexpr int kTileLoadsM = kTileLoads + MPW;   // with the mask tile
+  constexpr int kWaitAllButOneTileM = (kTileLoadsM & 15) | ((kTileLoadsM >> 4) << 14) | (7 << 4) | (15 << 8);
+  // mask staging: lane offsets (row in the offset register, which the buffer bound checks: rows
+  // at or past Nq, and bytes past the end of the mask, read as 0)
+  const bool use_lds_mask = MASK && p.mask_lds;
+  auto msw = [](int r) { return (r / M_RPL) % M_CPR; };
+  const int mrow0 = wave * M_RPI + lane / M_CPR;
+  const uint32_t mo0 = (uint32_t)mrow0 * (uint32_t)p.Nkv + 16u * (uint32_t)((lane % M_CPR) ^ msw(mrow0));
+  const uint32_t m_step = (uint32_t)(WAVES * M_RPI) * (uint32_t)p.Nkv;
   // the LDS destination goes to M0, which must be provably wave-uniform
   const int wave_lds = __builtin_amdgcn_readfirstlane(wave * 1024);
   auto issue_tile = [&](int t, int stage) {
@@ -192,6 +215,17 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
         const uint32_t vo = (uint32_t)(((int64_t)rr * row_stride + 8 * (ld_pc ^ v_swz<RPB, VSWZ_BITS>(row))) * 2);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kdst + jj * WAVES * 1024), 16, ko, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + jj * WAVES * 1024), 16, vo, 0, 0, 0);
+      }
+    }
+    if constexpr (MASK) {
+      if (use_lds_mask) {
+        uint8_t* mdst = lds + M_OFS + stage * MTILE + wave_lds;
+        const int64_t mbase = (int64_t)q_block0 * p.Nkv + k0;
+        const uint32_t mbytes = (uint32_t)((int64_t)p.Nq * p.Nkv - mbase);   // to the end of the mask
+        __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc((void*)(p.mask + mbase), 0, mbytes, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < MPW; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (__attribute__((address_space(3))) void*)(mdst + i * WAVES * 1024), 16, mo0 + i * m_step, 0, 0, 0);
       }
     }
   };
@@ -234,6 +268,13 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
     for (int ks = 0; ks < KSTEPS; ++ks)
       kaddr[ks] = lds + K_OFS + krow * RB + 16 * ((2 * ks + (lane >> 5)) ^ ksw);
   }
+  // mask bytes of this lane's query row: chunk c (keys 16c .. 16c+15 of the tile), half kl
+  const uint8_t* maddr[MASK ? M_CPR : 1];
+  if constexpr (MASK) {
+    const int rl = wave * kRowsPerWave + (lane & 31);
+#pragma unroll
+    for (int c = 0; c < M_CPR; ++c) maddr[c] = lds + M_OFS + rl * BN + 16 * (c ^ msw(rl)) + kl;
+  }
   const uint8_t* vaddr[DT];
   const int g = lane >> 4, li = lane & 15;
   const bool dpad = (D < 32) && ((g & 1) != 0);    // O^T rows D..31 for D = 16: zero operand
@@ -263,8 +304,12 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
     // tile t resident for every wave (its LDS-DMA loads are counted by vmcnt, which the
     // barrier's own fence does not wait for; with three stages the loads of tile t+1, issued
     // after it, may stay in flight); every wave done with tile t-1, whose stage is refilled next
-    if (NSTAGE == 3 && t + 1 < ntiles) __builtin_amdgcn_s_waitcnt(kWaitAllButOneTile);
-    else __builtin_amdgcn_s_waitcnt(0);
+    if (NSTAGE == 3 && t + 1 < ntiles) {
+      if (use_lds_mask) __builtin_amdgcn_s_waitcnt(kWaitAllButOneTileM);
+      else __builtin_amdgcn_s_waitcnt(kWaitAllButOneTile);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
     __syncthreads();
     if (t + NSTAGE - 1 < ntiles) issue_tile(t + NSTAGE - 1, (S + NSTAGE - 1) % NSTAGE);
 
@@ -323,7 +368,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
         for (int hf = 0; hf < 2; ++hf) {
           const int key0 = k0 + 32 * mt + 16 * hf + kl;   // 8 consecutive keys
           uint32_t lo = 0, hi = 0;
-          if (p.mask_vec && key0 + 8 <= p.Nkv) {
+          if (use_lds_mask) {
+            const u32x2 w = *reinterpret_cast<const u32x2*>(maddr[2 * mt + hf] + S * MTILE);
+            lo = w[0]; hi = w[1];
+          } else if (p.mask_vec && key0 + 8 <= p.Nkv) {
             u32x2 w = *reinterpret_cast<const u32x2*>(mrow + key0);
             lo = w[0]; hi = w[1];
           } else {
@@ -404,7 +452,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
     auto tile_body = [&](auto masked_c) {
       u32x4 va[2][DT];
       u32x4 pb[2];
-      if constexpr (D <= 128 && MT >= 2) {
+      // (D = 256 with a mask measured faster one block at a time: its mask reads crowd the
+      // pipelined form's registers)
+      if constexpr (MT >= 2 && (D <= 128 || !MASK)) {
         // Software pipeline over the MT blocks of the tile: phase k issues the matrix work
         // S_{k+1} = K_{k+1} Q^T and O += V_{k-1} P_{k-1} and, on the vector ALUs meanwhile,
         // softmax(S_k), which depends on neither:
@@ -445,7 +495,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
             s_cur = s_nxt;
           }
         }
-      } else {                    // one block at a time (BN = 32, D = 256)
+      } else {                    // one block at a time (BN = 32; D = 256 with a mask)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           u32x4 kfa[KSTEPS];

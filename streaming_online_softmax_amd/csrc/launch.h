@@ -23,6 +23,8 @@ struct FwdParams {
   int chunk;            // keys per partition (split)
   int n_qblocks;        // ceil(Nq / query rows per workgroup); set by the launcher
   int mask_vec;         // mask rows may be read 8 bytes at a time
+  int mask_lds;         // mask tiles may be staged into LDS 16 bytes at a time (row starts
+                        // 16-byte aligned, (Nq + 256) * Nkv < 2^32)
   float scale_log2;     // log2(e) / sqrt(D)
 };
 

@@ -377,6 +377,44 @@ def test_mask_ragged_small(sa, D, BN):
         _compare(out.reshape(-1, D), lse.reshape(-1), ref, ref_lse, "f16", f"mask D={D} causal={causal}")
 
 
+@pytest.mark.parametrize("D,BN", [(16, 32), (32, 64), (64, 32), (64, 64), (128, 64), (256, 64)])
+def test_mask_staged_matches_direct(sa, D, BN):
+    """Mask tiles staged through LDS (rows 16-byte aligned) give bitwise the results of the mask
+    read straight from global memory (the same bytes 8 bytes off alignment), for attn_fwd and the
+    split producer, and match the oracle; N = 400 leaves a ragged last key tile and a partial
+    query block."""
+    rng = si.rng_for(89, D + BN)
+    N, H = 400, 2
+    q, k, v = (si.cast(x, "bf16") for x in si.draw_qkv(rng, (1, N, H, D), (1, N, H, D)))
+    mask, _ = si.bernoulli_mask(rng, N, N, 4)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    m16 = torch.from_numpy(mask).to(DEV)
+    buf = torch.zeros(N * N + 8, dtype=torch.uint8, device=DEV)
+    m8 = buf[8:].view(N, N)
+    m8.copy_(m16)
+    assert m16.data_ptr() % 16 == 0 and m8.data_ptr() % 16 == 8
+    for causal in (False, True):
+        o1, l1 = sa.fwd(qd, kd, vd, causal=causal, mask=m16, block_n=BN)
+        o2, l2 = sa.fwd(qd, kd, vd, causal=causal, mask=m8, block_n=BN)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"staged != direct (causal={causal})"
+        ref, ref_lse = oracle.attn_dense(q, k, v, causal=causal, mask=mask)
+        _compare(o1.reshape(-1, D), l1.reshape(-1), ref, ref_lse, "bf16", f"staged mask D={D} causal={causal}")
+    if BN == 64:
+        # five partitions of 80 keys (a multiple of 16: staged) against the same unaligned
+        p1 = sa.splitk(qd, kd, vd, 5, causal=True, mask=m16, combine=False)
+        p2 = sa.splitk(qd, kd, vd, 5, causal=True, mask=m8, combine=False)
+        torch.cuda.synchronize()
+        assert torch.equal(p1[0], p2[0]) and torch.equal(p1[1], p2[1]), "split: staged != direct"
+        ref_op, ref_lp = oracle.splitk(q, k, v, 5, causal=True, mask=mask)
+        for pp in range(5):
+            _compare(p1[0][pp].reshape(-1, D), None, ref_op[pp], ref_lp[pp], "bf16", f"staged mask o_partial p={pp}")
+            lp = p1[1][pp].reshape(-1).cpu().numpy().astype(np.float64)
+            fin = np.isfinite(ref_lp[pp])
+            assert np.all(lp[~fin] == -np.inf)
+            np.testing.assert_allclose(lp[fin], ref_lp[pp][fin], rtol=1e-4, atol=1e-4)
+
+
 # ---------------------------------------------------------------------------------------------
 # the combine on its own: static-P and runtime-P instantiations, every output dtype
 # ---------------------------------------------------------------------------------------------
