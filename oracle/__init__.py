@@ -5,7 +5,7 @@ import this package.  It shares no code with the HIP path and the HIP path never
 
 The arithmetic lives in ``oracle.c`` (plain C, double precision, OpenMP over query rows); this
 module only marshals arguments through ctypes.  Every function names the page passage it
-follows in the C source.  Inputs are torch CPU tensors (float32, bfloat16 or float16) or numpy
+follows in the C source.  Inputs are torch CPU tensors (float32, bfloat16, float16 or float64) or numpy
 float32 arrays; they are widened to double exactly inside the C code.  Outputs are numpy float64.
 
 Functions:
@@ -16,7 +16,9 @@ Functions:
     combine_log2       O3b the LSE-weighted split-K combine, base 2
     splitk             O3c split-K workspace (locally normalised O_p/l_p, base-2 LSE)
     round_bits         O4  round-to-nearest-even float32 -> bf16 / f16 bits
-    decode_bits            exact widening of bf16 / f16 bits
+    round_fp8_bits     O6  round-to-nearest-even, saturating float32 -> E4M3 / E5M2 codes
+    decode_bits            exact widening of bf16 / f16 bits and E4M3 / E5M2 codes
+    attn_dense_fp8v    O1  with V given as E4M3 codes times a scale
 """
 import ctypes
 import os
@@ -29,7 +31,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, F16 = 0, 1, 2
+F32, BF16, F16, E4M3, E5M2, F64 = 0, 1, 2, 3, 4, 5
 NO_NUMERATOR_RESCALE, SAME_BOUNDARY_BF16, SAME_BOUNDARY_F16 = 1, 2, 4
 
 _lib = None
@@ -65,6 +67,8 @@ def lib():
         L.oracle_splitk.argtypes = [vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, vp, i64, dp, dp]
         L.oracle_round_array.argtypes = [vp, i64, i32, vp]
         L.oracle_round_array.restype = None
+        L.oracle_round_fp8_array.argtypes = [vp, i64, i32, vp]
+        L.oracle_round_fp8_array.restype = None
         L.oracle_decode.argtypes = [vp, i32, i64, dp]
         L.oracle_softmax_rows.argtypes = [vp, i32, i64, i64, dp]
         L.oracle_softmax_rows.restype = None
@@ -76,7 +80,7 @@ def lib():
 
 def _as_cpu_tensor(x):
     if isinstance(x, np.ndarray):
-        x = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+        x = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64 if x.dtype == np.float64 else np.float32))
     x = x.detach()
     if x.device.type != "cpu":
         x = x.cpu()
@@ -90,6 +94,8 @@ def _dtype_code(t):
         return BF16
     if t.dtype == torch.float16:
         return F16
+    if t.dtype == torch.float64:
+        return F64
     raise TypeError(f"oracle: unsupported element type {t.dtype}")
 
 
@@ -228,11 +234,32 @@ def round_bits(x, target):
 
 
 def decode_bits(bits, dtype):
-    """Exact widening of uint16 bf16 ('bf16') or float16 ('f16') bit patterns to float64."""
-    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    """Exact widening to float64 of uint16 bf16 ('bf16') / float16 ('f16') bit patterns, or of
+    uint8 E4M3 ('e4m3') / E5M2 ('e5m2') codes."""
+    code = {"bf16": BF16, "f16": F16, "e4m3": E4M3, "e5m2": E5M2}[dtype]
+    bits = np.ascontiguousarray(bits, dtype=np.uint8 if code in (E4M3, E5M2) else np.uint16)
     out = np.zeros(bits.shape, np.float64)
-    lib().oracle_decode(_ptr(bits), BF16 if dtype == "bf16" else F16, bits.size, _ptr(out))
+    lib().oracle_decode(_ptr(bits), code, bits.size, _ptr(out))
     return out
+
+
+def round_fp8_bits(x, target):
+    """O6. float32 array -> uint8 codes, round to nearest even with saturation to the largest
+    finite value, E4M3 ('e4m3') or E5M2 ('e5m2')."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.zeros(x.shape, np.uint8)
+    lib().oracle_round_fp8_array(_ptr(x), x.size, E4M3 if target == "e4m3" else E5M2, _ptr(out))
+    return out
+
+
+def attn_dense_fp8v(q, k, v_codes, v_scale, causal=False, mask=None, rows=None):
+    """O1 with V given as E4M3 codes and a scale: the values the kernel consumes are
+    decode(v_codes) * v_scale (exact in float64); q and k (bf16 / f16) widen exactly."""
+    qd = _as_cpu_tensor(q).to(torch.float64)
+    kd = _as_cpu_tensor(k).to(torch.float64)
+    codes = v_codes.cpu().numpy() if isinstance(v_codes, torch.Tensor) else np.asarray(v_codes)
+    vd = torch.from_numpy(decode_bits(codes, "e4m3") * float(v_scale))
+    return attn_dense(qd, kd, vd, causal=causal, mask=mask, rows=rows)
 
 
 def num_threads():

@@ -16,8 +16,9 @@
  *   [SK]  Modular MAX Mojo module "fa4_splitk_combine": workspace layout and the per-row-head
  *         combine formulas.
  *
- * Everything is computed in double precision.  Inputs arrive as float32, bfloat16 or float16
- * element arrays and are widened to double exactly (every such value is a double).
+ * Everything is computed in double precision.  Inputs arrive as float32, bfloat16, float16,
+ * 8-bit float (E4M3 / E5M2) or float64 element arrays and are widened to double exactly (every
+ * such value is a double).
  *
  * Tensor layouts: q is [B, Nq, H, D]; k and v are [B, Nkv, H, D], D fastest.  A row-head index
  * rh = (b * Nq + i) * H + h names one query row of one head.  The optional mask is a row-major
@@ -31,7 +32,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2, OR_E4M3 = 3, OR_E5M2 = 4, OR_F64 = 5 };
 enum { OR_NO_NUMERATOR_RESCALE = 1, OR_SAME_BOUNDARY_BF16 = 2, OR_SAME_BOUNDARY_F16 = 4 };
 
 /* ---------------------------------------------------------------------------------------------
@@ -52,8 +53,32 @@ static double decode_bf16_bits(uint16_t b) {
   memcpy(&x, &u, 4);
   return (double)x;
 }
+/* 8-bit floats ([TR] Logical types and register packing: Float8E4M3, Float8E5M2), decoded from
+ * their fields.  E4M3: sign, 4-bit exponent (bias 7), 3-bit fraction; exponent 0 is subnormal
+ * (f * 2^-9); there are no infinities and S.1111.111 is NaN, so the largest finite value is
+ * 1.75 * 2^8 = 448.  E5M2: sign, 5-bit exponent (bias 15), 2-bit fraction, IEEE-like (exponent 0
+ * subnormal f * 2^-16; exponent 31: infinity if f = 0, else NaN). */
+static double decode_e4m3_bits(uint8_t c) {
+  int sign = c >> 7, e = (c >> 3) & 15, f = c & 7;
+  double mag;
+  if (e == 15 && f == 7) mag = NAN;
+  else if (e == 0) mag = ldexp((double)f, -9);
+  else mag = ldexp(1.0 + f / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+static double decode_e5m2_bits(uint8_t c) {
+  int sign = c >> 7, e = (c >> 2) & 31, f = c & 3;
+  double mag;
+  if (e == 31) mag = f ? NAN : INFINITY;
+  else if (e == 0) mag = ldexp((double)f, -16);
+  else mag = ldexp(1.0 + f / 4.0, e - 15);
+  return sign ? -mag : mag;
+}
 static double load_elem(const void* base, int64_t idx, int dtype) {
   if (dtype == OR_F32) return (double)((const float*)base)[idx];
+  if (dtype == OR_F64) return ((const double*)base)[idx];
+  if (dtype == OR_E4M3) return decode_e4m3_bits(((const uint8_t*)base)[idx]);
+  if (dtype == OR_E5M2) return decode_e5m2_bits(((const uint8_t*)base)[idx]);
   uint16_t bits = ((const uint16_t*)base)[idx];
   return dtype == OR_BF16 ? decode_bf16_bits(bits) : decode_f16_bits(bits);
 }
@@ -128,6 +153,65 @@ void oracle_round_array(const float* x, int64_t n, int target_dtype, uint16_t* o
   fmt_t f = target_dtype == OR_BF16 ? FMT_BF16 : FMT_F16;
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) out[i] = round_rne(x[i], f);
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * O6. Round-to-nearest-even conversion of a float32 to E4M3 / E5M2 bits with saturation to the
+ * largest finite value ([TR] Logical types and register packing: the 8-bit float types convert
+ * from FP32 to nearest even and saturate to the largest finite value).  Same construction as
+ * O4: the two neighbouring values at the input's binade spacing (exponent range unbounded
+ * above), the nearer, ties to the even last significand bit; a result beyond the largest finite
+ * value (448 for E4M3, 57344 for E5M2), and an infinite input, become that value with the
+ * input's sign.  Signed zeros are kept, subnormals are not flushed, NaN gives a NaN.
+ * ------------------------------------------------------------------------------------------- */
+typedef struct { int p, emin, ebits; double maxfin; } fmt8_t;
+static const fmt8_t FMT_E4M3 = {4, -6, 4, 448.0};
+static const fmt8_t FMT_E5M2 = {3, -14, 5, 57344.0};
+
+static uint8_t encode8(double mag, int sign, fmt8_t f) {
+  /* mag is finite and exactly representable in f */
+  int mbits = f.p - 1, bias = (1 << (f.ebits - 1)) - 1;
+  uint32_t e_field = 0, m_field = 0;
+  if (mag != 0.0) {
+    int e;
+    frexp(mag, &e);
+    int E = e - 1;
+    if (E < f.emin) {
+      m_field = (uint32_t)ldexp(mag, -(f.emin - mbits));
+    } else {
+      e_field = (uint32_t)(E + bias);
+      m_field = (uint32_t)(ldexp(mag, -E) * (double)(1u << mbits)) - (1u << mbits);
+    }
+  }
+  return (uint8_t)((sign << 7) | (e_field << mbits) | m_field);
+}
+
+static uint8_t round_fp8(float xf, fmt8_t f) {
+  double x = (double)xf;
+  int sign = signbit(x) ? 1 : 0;
+  if (isnan(x)) return (uint8_t)0x7f;                 /* a NaN in both formats */
+  double a = fabs(x);
+  if (isinf(a)) return encode8(f.maxfin, sign, f);
+  if (a == 0.0) return (uint8_t)(sign << 7);
+  int e;
+  frexp(a, &e);
+  int E = e - 1;
+  if (E < f.emin) E = f.emin;
+  double ulp = ldexp(1.0, E - (f.p - 1));
+  double lo = floor(a / ulp) * ulp;
+  double hi = lo + ulp;
+  double pick;
+  if (a - lo < hi - a) pick = lo;
+  else if (hi - a < a - lo) pick = hi;
+  else pick = (fmod(lo / ulp, 2.0) == 0.0) ? lo : hi;
+  if (pick > f.maxfin) pick = f.maxfin;               /* saturate to finite */
+  return encode8(pick, sign, f);
+}
+
+void oracle_round_fp8_array(const float* x, int64_t n, int target_dtype, uint8_t* out) {
+  fmt8_t f = target_dtype == OR_E4M3 ? FMT_E4M3 : FMT_E5M2;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = round_fp8(x[i], f);
 }
 
 /* Same-boundary rounding of a weight: the caller passes the weight already rounded to float32

@@ -449,6 +449,122 @@ def test_decode_every_pattern():
 
 
 # ------------------------------------------------------------------------------------------
+# O6: 8-bit floats (Tylo "Register fragments and logical axes", "Logical types and register
+# packing": Float8E4M3 / Float8E5M2, round to nearest even, saturate to the largest finite value)
+# ------------------------------------------------------------------------------------------
+_TORCH_FP8 = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+_FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+
+
+def test_fp8_decode_every_code_matches_library():
+    """All 256 codes of each format widen exactly as torch's float8 types do."""
+    codes = np.arange(256, dtype=np.uint8)
+    for fmt, tdt in _TORCH_FP8.items():
+        got = oracle.decode_bits(codes, fmt)
+        ref = torch.from_numpy(codes).view(tdt).double().numpy()
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan)
+        np.testing.assert_array_equal(got[~nan], ref[~nan])
+        np.testing.assert_array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    # format facts: E4M3 has one NaN pattern per sign and no infinities, so its largest finite
+    # value is 1.75 * 2^8; E5M2 keeps IEEE infinities
+    e4 = oracle.decode_bits(codes, "e4m3")
+    assert e4[0x7E] == 448.0 and np.isnan(e4[0x7F]) and np.isnan(e4[0xFF]) and not np.isinf(e4).any()
+    assert e4[0x01] == 2.0 ** -9 and e4[0x08] == 2.0 ** -6 and e4[0x38] == 1.0
+    e5 = oracle.decode_bits(codes, "e5m2")
+    assert e5[0x7B] == 57344.0 and e5[0x7C] == np.inf and e5[0xFC] == -np.inf and e5[0x01] == 2.0 ** -16
+
+
+def _brute_force_fp8(x, fmt):
+    """Nearest finite code by exhaustive search over the decoded table, ties to the code whose
+    last fraction bit is 0, then saturation; NaN -> NaN."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.decode_bits(codes, fmt)
+    fin = np.isfinite(vals)
+    cand, cv = codes[fin], vals[fin]
+    out = np.zeros(x.shape, np.float64)
+    for i, xv in enumerate(x.astype(np.float64)):
+        if np.isnan(xv):
+            out[i] = np.nan
+            continue
+        xc = float(np.clip(xv, -_FP8_MAX[fmt], _FP8_MAX[fmt]))
+        d = np.abs(cv - xc)
+        best = np.nonzero(d == d.min())[0]
+        if best.size > 1:
+            best = best[(cand[best] & 1) == 0]
+        out[i] = cv[best[0]] if cv[best[0]] != 0 else np.copysign(0.0, xv)   # a zero keeps the sign
+    return out
+
+
+def test_fp8_round_brute_force_nearest():
+    """O6 against an exhaustive nearest search: random values over every binade of both formats
+    (subnormal range and beyond the largest finite value included), exact ties, signed zero."""
+    rng = np.random.default_rng(12)
+    for fmt in ("e4m3", "e5m2"):
+        vals = oracle.decode_bits(np.arange(256, dtype=np.uint8), fmt)
+        fin = np.sort(np.unique(vals[np.isfinite(vals)]))
+        mids = (fin[1:] + fin[:-1]) / 2                       # every exact tie (exact in float32)
+        x = np.concatenate([
+            np.exp2(rng.uniform(-20, 18, 3000)) * rng.choice([-1, 1], 3000),
+            mids, np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+            np.nextafter(mids.astype(np.float32), np.float32(-np.inf)),
+            [0.0, -0.0, np.inf, -np.inf, np.nan, 1e30, -1e30]]).astype(np.float32)
+        got = oracle.decode_bits(oracle.round_fp8_bits(x, fmt), fmt)
+        ref = _brute_force_fp8(x, fmt)
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan)
+        np.testing.assert_array_equal(got[~nan], ref[~nan])
+        np.testing.assert_array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_fp8_round_in_range_matches_library_and_saturates():
+    """Within the finite range O6 equals torch's float8 conversion (which rounds to nearest even
+    but does not saturate); beyond it, and for infinities, the result is the largest finite value
+    of the input's sign (E4M3: 464 is the tie between 448 and the missing 480 and goes to 448)."""
+    rng = np.random.default_rng(13)
+    for fmt, tdt in _TORCH_FP8.items():
+        mx = _FP8_MAX[fmt]
+        u = rng.integers(0, 1 << 32, 1 << 20, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        x = u[np.isfinite(u) & (np.abs(u) <= mx)]
+        got = oracle.round_fp8_bits(x, fmt)
+        ref = torch.from_numpy(x).to(tdt).view(torch.uint8).numpy()
+        np.testing.assert_array_equal(got, ref)
+        big = np.array([np.inf, 1e30, 2 * mx, mx * 1.0625, -np.inf, -1e30, -2 * mx], np.float32)
+        dec = oracle.decode_bits(oracle.round_fp8_bits(big, fmt), fmt)
+        np.testing.assert_array_equal(dec, np.where(big > 0, mx, -mx))
+    tie = oracle.decode_bits(oracle.round_fp8_bits(np.array([464.0, 464.01, -464.0], np.float32), "e4m3"), "e4m3")
+    assert tie.tolist() == [448.0, 448.0, -448.0]
+
+
+def test_attn_dense_fp8v_definition():
+    """O1 with V as E4M3 codes times a scale: (a) equals O1 on the same values stored as bf16
+    (every E4M3 value with |v| <= 448 is a bf16 value), through a different decoder; (b) is linear
+    in the scale (out halves, LSE unchanged); (c) equals a numpy float64 softmax-weighted sum with
+    V decoded by torch's float8 type."""
+    rng = np.random.default_rng(14)
+    B, N, H, D = 1, 37, 2, 16
+    q = torch.from_numpy(rng.standard_normal((B, N, H, D)).astype(np.float32)).to(torch.bfloat16)
+    k = torch.from_numpy(rng.standard_normal((B, N, H, D)).astype(np.float32)).to(torch.bfloat16)
+    codes = oracle.round_fp8_bits(rng.standard_normal((B, N, H, D)).astype(np.float32), "e4m3")
+    v_bf16 = torch.from_numpy(oracle.decode_bits(codes, "e4m3").astype(np.float32)).to(torch.bfloat16)
+    for causal in (False, True):
+        o8, l8 = oracle.attn_dense_fp8v(q, k, codes, 1.0, causal=causal)
+        ob, lb = oracle.attn_dense(q, k, v_bf16, causal=causal)
+        np.testing.assert_allclose(o8, ob, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(l8, lb, rtol=0, atol=1e-14)
+        oh, lh = oracle.attn_dense_fp8v(q, k, codes, 0.5, causal=causal)
+        np.testing.assert_allclose(oh, 0.5 * o8, rtol=0, atol=1e-15)
+        np.testing.assert_array_equal(lh, l8)
+    vt = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    qd, kd = q.double().numpy(), k.double().numpy()
+    s = np.einsum("bihd,bjhd->bhij", qd, kd) / np.sqrt(D)
+    w = np.exp(s - s.max(-1, keepdims=True))
+    ref = np.einsum("bhij,bjhd->bihd", w / w.sum(-1, keepdims=True), vt * 0.25)
+    o, _ = oracle.attn_dense_fp8v(q, k, codes, 0.25)
+    np.testing.assert_allclose(o, ref.reshape(-1, D), rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------------------------------------
 # O5: standalone row softmax (Tylo "Register fragments and logical axes", "Worked softmax";
 # Tylo "Streaming attention and online state", "Online statistics")
 # ------------------------------------------------------------------------------------------
