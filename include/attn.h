@@ -20,7 +20,8 @@
  *   attn_softmax_rows        standalone row softmax (streaming, registers or three-pass)
  *                    with the all-masked conventions of Tylo.jl "Register fragments and
  *                    logical axes", section "Worked softmax".
- *   attn_round       FP32 -> bf16 / fp16 with the conversion the kernels apply to the
+ *   attn_fwd_fp8v    attn_fwd with V as E4M3 and P rounded to E4M3 for the FP8 matrix cores.
+ *   attn_round       FP32 -> bf16 / fp16 / E4M3 with the conversion the kernels apply to the
  *                    probabilities and to the output (exposed so it can be checked bit by bit).
  *
  * Conventions shared by every entry point
@@ -59,7 +60,12 @@ extern "C" {
 #define ATTN_ABI_VERSION 1
 #define ATTN_P_MAX 256 /* largest split count: one partition per MI355X compute unit */
 
-enum attn_dtype { ATTN_BF16 = 0, ATTN_FP16 = 1, ATTN_FP32 = 2 /* combine output only */ };
+enum attn_dtype {
+  ATTN_BF16 = 0,
+  ATTN_FP16 = 1,
+  ATTN_FP32 = 2,     /* combine / softmax only */
+  ATTN_FP8_E4M3 = 3  /* V of attn_fwd_fp8v; attn_round target */
+};
 
 enum attn_status {
   ATTN_OK = 0,
@@ -165,15 +171,18 @@ enum attn_softmax_method { ATTN_SOFTMAX_STREAMING = 0, ATTN_SOFTMAX_REGISTERS = 
 int attn_softmax_rows(const void* x, void* y, int64_t rows, int n, int dtype, int method, void* stream);
 
 /*
- * attn_round -- y[i] = x[i] rounded to bf16 or fp16, to nearest with ties to even, by the packed
- *   conversion the attention kernels use for the probabilities before the second product and for
- *   the stored output (Tylo.jl "Streaming attention and online state", section "Same-lane
- *   conversion": round to nearest even, signed zeros and infinities kept, NaN stays NaN, no
- *   saturation and no flush to zero; Tylo.jl "Register fragments and logical axes", section
- *   "Logical types and register packing": the packed word).  Values beyond the largest finite value become +-inf; +-0 and +-inf keep their
- *   sign; NaN gives a NaN.
- *   x      n FP32 values (device, 4-byte aligned);  y  n 16-bit results (device, 2-byte aligned).
- *   dtype  ATTN_BF16 or ATTN_FP16.  n = 0 enqueues nothing.
+ * attn_round -- y[i] = x[i] rounded to bf16, fp16 or E4M3, to nearest with ties to even, by the
+ *   packed conversion the attention kernels use for the probabilities before the second product
+ *   and for the stored output.
+ *   bf16 / fp16 (Tylo.jl "Streaming attention and online state", section "Same-lane conversion":
+ *   signed zeros and infinities kept, NaN stays NaN, no saturation and no flush to zero; Tylo.jl
+ *   "Register fragments and logical axes", section "Logical types and register packing": the
+ *   packed word): values beyond the largest finite value become +-inf.
+ *   ATTN_FP8_E4M3 (the same section's 8-bit rule): saturation to +-448 instead, infinities give
+ *   +-448, subnormals kept, NaN gives a NaN code.
+ *   x      n FP32 values (device, 4-byte aligned);  y  n results of dtype's size (device, aligned
+ *          to it).
+ *   dtype  ATTN_BF16, ATTN_FP16 or ATTN_FP8_E4M3.  n = 0 enqueues nothing.
  *   Errors: ATTN_E_SHAPE (n < 0), ATTN_E_NULL, ATTN_E_UNSUPPORTED (dtype), ATTN_E_ALIGN.
  */
 int attn_round(const float* x, void* y, int64_t n, int dtype, void* stream);
@@ -192,6 +201,26 @@ struct attn_fwd_args {
   int block_n;         /* key-tile width: 0 = library default, else 32 or 64 (32 only for D <= 64) */
 };
 int attn_fwd_ex(const struct attn_fwd_args* a, void* stream);
+
+/*
+ * attn_fwd_fp8v -- attn_fwd with V in 8-bit floating point and the second product (P.V) on the
+ *   FP8 matrix cores.  Element types from Tylo.jl "Register fragments and logical axes", section
+ *   "Logical types and register packing" (Float8E4M3: four 8-bit values per 32-bit register;
+ *   FP32 conversion to nearest even, saturating to the largest finite value); the recurrence is
+ *   attn_fwd's.  The value of V[b, j, h, d] is decode_E4M3(v[b, j, h, d]) * v_scale.  Each
+ *   probability is rounded from FP32 to E4M3 (nearest even; it is at most 256, inside E4M3's
+ *   range) before the product, while the denominator l keeps the unrounded FP32 weights (the
+ *   rounding-before-PV rule of Tylo.jl "Streaming attention and online state", section
+ *   "Attention as a consumer").  Q K^T stays in q/k's type.
+ *   q, k, out  [B, N, H, D] bf16 or fp16 (dtype), 16-byte aligned; D must be 128.
+ *   v          [B, N, H, D] E4M3 codes, one byte per element (S.EEEE.MMM, bias 7, no
+ *              infinities, S.1111.111 = NaN), 16-byte aligned; codes must be finite.
+ *   v_scale    finite FP32 scale of V (1.0 when V is stored unscaled).
+ *   lse, causal, mask, stream: as attn_fwd (lse is the LSE of the scores, unaffected by v_scale).
+ *   Errors: those of attn_fwd; ATTN_E_UNSUPPORTED also for D != 128 or a non-finite v_scale.
+ */
+int attn_fwd_fp8v(const void* q, const void* k, const uint8_t* v, float v_scale, void* out, float* lse, int B,
+                  int H, int N, int D, int causal, const uint8_t* mask, int dtype, void* stream);
 
 /* Message describing the calling thread's last non-OK return ("" if none). */
 const char* attn_last_error(void);

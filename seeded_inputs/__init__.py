@@ -30,13 +30,15 @@ MASKED = dict(name="masked causal B1 H16 N16384 D256 bf16", B=1, H=16, N=16384, 
 SOFTMAX = dict(name="row softmax 32768 rows x 4096 logits fp32", rows=32768, n=4096, dtype="f32")
 SOFTMAX_WIDE = dict(name="row softmax 4096 rows x 32768 logits fp32", rows=4096, n=32768, dtype="f32")
 
+FP8V = dict(name="causal prefill B4 H32 N4096 D128, bf16 Q/K, E4M3 V", B=4, H=32, N=4096, D=128, causal=True)
+
 SWEEP_N = (1, 17, 1000, 2047, 2048)
 SWEEP_D = (16, 32, 64)
 SWEEP_DTYPES = ("bf16", "f16")
 SWEEP_BN = (32, 64)
 SWEEP_VARIANTS = ("normal", "large", "uniform")
 
-CFG_SMALL, CFG_SWEEP, CFG_PREFILL, CFG_DECODE, CFG_MASKED, CFG_SOFTMAX = 1, 2, 3, 4, 5, 6
+CFG_SMALL, CFG_SWEEP, CFG_PREFILL, CFG_DECODE, CFG_MASKED, CFG_SOFTMAX, CFG_FP8V = 1, 2, 3, 4, 5, 6, 7
 
 
 def rng_for(cfg, case):
@@ -72,6 +74,22 @@ def cast(x, dtype):
     """float32 numpy -> torch CPU tensor of the kernel dtype (round to nearest even)."""
     t = torch.from_numpy(np.ascontiguousarray(x))
     return t.to(DTYPES[dtype]) if dtype != "f32" else t.clone()
+
+
+def cast_e4m3(x):
+    """float32 numpy -> uint8 torch CPU tensor of E4M3 codes (torch's float8_e4m3fn conversion,
+    round to nearest even; the draws here stay far inside its finite range)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def fp8v_inputs(B=None, H=None, N=None, case=0, dtype="bf16"):
+    """q, k in dtype and v as E4M3 codes, all [B, N, H, D], drawn like the prefill workload."""
+    s = FP8V
+    B, H, N = B or s["B"], H or s["H"], N or s["N"]
+    rng = rng_for(CFG_FP8V, case)
+    q, k, v = draw_qkv(rng, (B, N, H, s["D"]), (B, N, H, s["D"]))
+    return cast(q, dtype), cast(k, dtype), cast_e4m3(v)
 
 
 def bernoulli_mask(rng, Nq, Nkv, n_full_rows, row_block=1024):

@@ -12,12 +12,13 @@ Entry points (same names as the C ABI in include/attn.h):
                           mask=None, stream=None)
     attn_combine(o_partial, lse_partial, out, lse_out=None, stream=None)
     attn_softmax_rows(x, y, method=SOFTMAX_STREAMING, stream=None)   (x, y: [..., n])
-    attn_round(x, y, stream=None)    (x float32, y bf16/fp16, same number of elements)
+    attn_fwd_fp8v(q, k, v, v_scale, out, lse=None, causal=False, mask=None, stream=None)
+    attn_round(x, y, stream=None)    (x float32, y bf16/fp16/E4M3, same number of elements)
     attn_last_error(), attn_abi_version()
 Tensors are torch tensors on the GPU, contiguous, laid out as the header states
 (q/out [B, Nq, H, D]; k/v [B, Nkv, H, D]; o_partial [P, B*Nq, H, D]; lse_partial [P, B*Nq, H];
 tickets int32 [B*Nq*H], zero before the first call and left zero by every call).
-Allocating helpers fwd(), splitk(), splitk_fused() and combine() return fresh outputs.
+Allocating helpers fwd(), fwd_fp8v(), splitk(), splitk_fused() and combine() return fresh outputs.
 """
 import ctypes
 import os
@@ -29,7 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "attn.h")
 
-ATTN_BF16, ATTN_FP16, ATTN_FP32 = 0, 1, 2
+ATTN_BF16, ATTN_FP16, ATTN_FP32, ATTN_FP8_E4M3 = 0, 1, 2, 3
 STATUS = {0: "ATTN_OK", 1: "ATTN_E_NULL", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUPPORTED",
           4: "ATTN_E_ALIGN", 5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
 P_MAX = 256
@@ -74,6 +75,8 @@ def _load():
     L.attn_softmax_rows.argtypes = [vp, vp, ctypes.c_int64, i32, i32, i32, vp]
     L.attn_softmax_rows.restype = i32
     L.attn_round.argtypes = [vp, vp, ctypes.c_int64, i32, vp]
+    L.attn_fwd_fp8v.argtypes = [vp, vp, vp, ctypes.c_float, vp, vp, i32, i32, i32, i32, i32, vp, i32, vp]
+    L.attn_fwd_fp8v.restype = i32
     L.attn_round.restype = i32
     L.attn_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     L.attn_combine.restype = i32
@@ -168,11 +171,30 @@ def attn_softmax_rows(x, y, method=SOFTMAX_STREAMING, stream=None):
     _check(lib().attn_softmax_rows(_ptr(x), _ptr(y), rows, n, _dtype_code(x), int(method), _stream(stream)))
 
 
+def _fp8_code(t):
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return ATTN_FP8_E4M3
+    raise AttnError(3, f"E4M3 data must be uint8 codes or torch.float8_e4m3fn (got {t.dtype})")
+
+
 def attn_round(x, y, stream=None):
-    """y (bf16 or fp16) = x (fp32) rounded to nearest even by the kernels' packed conversion."""
+    """y = x (fp32) rounded to nearest even by the kernels' packed conversion: bf16 / fp16, or
+    E4M3 (saturating) when y is uint8 or float8_e4m3fn."""
     if x.dtype != torch.float32 or x.numel() != y.numel():
         raise AttnError(2, "x must be float32 with as many elements as y")
-    _check(lib().attn_round(_ptr(x), _ptr(y), x.numel(), _dtype_code(y), _stream(stream)))
+    code = _fp8_code(y) if y.element_size() == 1 else _dtype_code(y)
+    _check(lib().attn_round(_ptr(x), _ptr(y), x.numel(), code, _stream(stream)))
+
+
+def attn_fwd_fp8v(q, k, v, v_scale, out, lse=None, causal=False, mask=None, stream=None):
+    """attn_fwd with V as E4M3 codes (uint8 or float8_e4m3fn, [B, N, H, D]) of value code * v_scale;
+    P is rounded to E4M3 for the FP8 second product.  D must be 128."""
+    B, N, H, D = q.shape
+    _fp8_code(v)
+    if tuple(v.shape) != (B, N, H, D):
+        raise AttnError(2, f"v must be [B, N, H, D] = {(B, N, H, D)} (got {tuple(v.shape)})")
+    _check(lib().attn_fwd_fp8v(_ptr(q), _ptr(k), _ptr(v), float(v_scale), _ptr(out), _ptr(lse), B, H, N, D,
+                               int(bool(causal)), _ptr(mask), _dtype_code(q), _stream(stream)))
 
 
 # ---- allocating helpers -------------------------------------------------------------------
@@ -180,6 +202,13 @@ def fwd(q, k, v, causal=False, mask=None, block_n=0, with_lse=True):
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if with_lse else None
     attn_fwd(q, k, v, out, lse, causal=causal, mask=mask, block_n=block_n)
+    return out, lse
+
+
+def fwd_fp8v(q, k, v, v_scale=1.0, causal=False, mask=None):
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn_fwd_fp8v(q, k, v, v_scale, out, lse, causal=causal, mask=mask)
     return out, lse
 
 

@@ -133,6 +133,31 @@ int attn_fwd_ex(const struct attn_fwd_args* a, void* stream) {
   return fwd_impl(a, (hipStream_t)stream);
 }
 
+int attn_fwd_fp8v(const void* q, const void* k, const uint8_t* v, float v_scale, void* out, float* lse, int B,
+                  int H, int N, int D, int causal, const uint8_t* mask, int dtype, void* stream) {
+  int rc = check_qkv(q, k, v, B, H, N, N, D, causal, dtype);
+  if (rc) return rc;
+  if (D != 128) return fail(ATTN_E_UNSUPPORTED, "attn_fwd_fp8v is built for D = 128 (got %d)", D);
+  if (!std::isfinite(v_scale)) return fail(ATTN_E_UNSUPPORTED, "v_scale must be finite");
+  if (!out) return fail(ATTN_E_NULL, "out must be a non-NULL device pointer");
+  if (!aligned(out, 16)) return fail(ATTN_E_ALIGN, "out must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(ATTN_E_ALIGN, "lse must be 4-byte aligned");
+  const int64_t nqb = ((int64_t)N + 255) / 256;
+  if (nqb * H * B > 0x7fffffffLL) return fail(ATTN_E_SHAPE, "grid too large");
+  attn::FwdParams p{};
+  p.q = q; p.k = k; p.v = v;
+  p.out = out; p.lse = lse;
+  p.mask = mask;
+  p.B = B; p.H = H; p.Nq = N; p.Nkv = N;
+  p.causal = causal;
+  p.P = 1; p.chunk = N;
+  p.mask_vec = mask && aligned(mask, 8) && (N % 8 == 0);
+  p.mask_lds = mask && aligned(mask, 16) && (N % 16 == 0) && ((int64_t)N + 256) * N < (1LL << 32);
+  p.scale_log2 = scale_log2(D);
+  p.v_scale = v_scale;
+  return hip_status(attn::launch_fwd_fp8v(p, dtype, (hipStream_t)stream), "attn_fwd_fp8v launch");
+}
+
 int attn_fwd_splitk(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
                     int Nq, int Nkv, int D, int causal, const uint8_t* mask, int P, float* o_partial,
                     float* lse_partial, int dtype, void* stream) {
@@ -220,9 +245,11 @@ int attn_round(const float* x, void* y, int64_t n, int dtype, void* stream) {
   if (n < 0) return fail(ATTN_E_SHAPE, "n must be >= 0 (got %lld)", (long long)n);
   if (n == 0) return ATTN_OK;
   if (!x || !y) return fail(ATTN_E_NULL, "x and y must be non-NULL device pointers");
-  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return fail(ATTN_E_UNSUPPORTED, "dtype %d not supported (bf16 or fp16)", dtype);
-  if (!aligned(x, 4) || !aligned(y, 2)) return fail(ATTN_E_ALIGN, "x must be 4-byte and y 2-byte aligned");
-  return hip_status(attn::launch_round(x, y, n, dtype == ATTN_BF16 ? 0 : 1, (hipStream_t)stream), "attn_round launch");
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16 && dtype != ATTN_FP8_E4M3)
+    return fail(ATTN_E_UNSUPPORTED, "dtype %d not supported (bf16, fp16 or E4M3)", dtype);
+  if (!aligned(x, 4) || !aligned(y, dtype == ATTN_FP8_E4M3 ? 1 : 2)) return fail(ATTN_E_ALIGN, "x must be 4-byte and y element-size aligned");
+  const int t = dtype == ATTN_BF16 ? 0 : (dtype == ATTN_FP16 ? 1 : 3);
+  return hip_status(attn::launch_round(x, y, n, t, (hipStream_t)stream), "attn_round launch");
 }
 
 int attn_combine(const float* o_partial, const float* lse_partial, void* out, float* lse_out, int P,

@@ -63,7 +63,9 @@ __device__ __forceinline__ int v_swz(int row) { return BITS ? 4 * ((row / RPB) &
 template <int S> using stage_t = std::integral_constant<int, S>;
 
 // WAVES waves of 32 query rows each; BN keys per tile.
-template <typename T, int D, int BN, bool MASK, bool SPLIT, int WAVES, int NSTAGES>
+// V8: V is E4M3 (one byte per element) and the second product runs on the FP8 matrix cores
+// (v_mfma_f32_32x32x64_f8f6f4, one 64-key tile per instruction), with P rounded to E4M3.
+template <typename T, int D, int BN, bool MASK, bool SPLIT, int WAVES, int NSTAGES, bool V8 = false>
 __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void attn_fwd_kernel(FwdParams p) {
   using E = elem<T>;
   constexpr int kBlockM = WAVES * kRowsPerWave;
@@ -92,6 +94,15 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   static_assert((WAVES * M_RPI / M_RPL) % M_CPR == 0, "mask swizzle independent of the instruction");
   static_assert(WAVES == 4 || WAVES == 8, "four or eight waves per workgroup");
   static_assert(TILE % 1024 == 0, "tile must be a whole number of 1 KiB wave loads");
+  // V tiles: 2 bytes per element, or 1 with V8.  V8 rows (D bytes, 8 chunks) are swizzled by
+  // chunk ^ ((row / 2) % 8), which spreads the 16 rows one byte-transposing read touches.
+  static_assert(!V8 || (D == 128 && BN == 64 && !SPLIT), "the FP8 second product is built for D = 128, 64-key tiles");
+  constexpr int RBV = V8 ? D : RB;      // bytes per V row in LDS
+  constexpr int TILEV = BN * RBV;
+  constexpr int NTV = TILEV / 1024;
+  constexpr int RPIV = 1024 / RBV;
+  constexpr int CHV = RBV / 16;
+  constexpr int PER_WAVE_V8 = (NTV + WAVES - 1) / WAVES;
   // LDS stages: tiles are loaded NSTAGE-1 ahead.  Three stages where one workgroup owns the CU
   // (eight waves), two otherwise.
   constexpr int NSTAGE = NSTAGES;
@@ -100,9 +111,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   // (block, key step, stage), which must fit the 16-bit DS offset.
   constexpr int K_OFS = 0, V_OFS = NSTAGE * TILE;
   static_assert((NSTAGE - 1) * TILE + (MT - 1) * 32 * RB < 65536, "K read offsets exceed the DS immediate");
-  static_assert((NSTAGE - 1) * TILE + (BN - 1) * RB < 65536, "V read offsets exceed the DS immediate");
+  static_assert((NSTAGE - 1) * TILEV + (BN - 1) * RBV < 65536, "V read offsets exceed the DS immediate");
 
-  constexpr int M_OFS = 2 * NSTAGE * TILE;
+  constexpr int M_OFS = NSTAGE * (TILE + TILEV);
   static_assert(M_OFS + NSTAGE * MTILE <= 160 * 1024, "LDS budget of one workgroup");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[M_OFS + NSTAGE * MTILE];
 
@@ -150,6 +161,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   const uint16_t* qbase = (const uint16_t*)p.q + ((int64_t)b * p.Nq * p.H + h) * D;
   const uint16_t* kbase = (const uint16_t*)p.k + ((int64_t)b * p.Nkv * p.H + h) * D;
   const uint16_t* vbase = (const uint16_t*)p.v + ((int64_t)b * p.Nkv * p.H + h) * D;
+  const uint8_t* vbase8 = (const uint8_t*)p.v + ((int64_t)b * p.Nkv * p.H + h) * D;   // V8
 
   // ---- direct global -> LDS staging (buffer_load ... lds).  Wave-instruction j of a tile fills
   //      LDS bytes [1024 j, 1024 j + 1024): lane l lands at row j*RPI + l/CH, physical chunk
@@ -169,8 +181,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   const uint32_t tile_bytes = (uint32_t)((int64_t)BN * row_stride * 2);
   // s_waitcnt immediate for "vmcnt <= the loads of one tile" (gfx9 encoding: vmcnt in bits 3:0
   // and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima, i.e. not waited for)
-  constexpr int kTileLoads = 2 * PER_WAVE;
+  constexpr int kTileLoads = PER_WAVE + (V8 ? PER_WAVE_V8 : PER_WAVE);
   static_assert(NSTAGE == 2 || NT % WAVES == 0, "three stages need the same load count in every wave");
+  static_assert(NSTAGE == 2 || !V8 || NTV % WAVES == 0, "three stages need the same load count in every wave");
   constexpr int kWaitAllButOneTile = (kTileLoads & 15) | ((kTileLoads >> 4) << 14) | (7 << 4) | (15 << 8);
   constexpr int kTileLoadsM = kTileLoads + MPW;   // with the mask tile
   constexpr int kWaitAllButOneTileM = (kTileLoadsM & 15) | ((kTileLoadsM >> 4) << 14) | (7 << 4) | (15 << 8);
@@ -186,7 +199,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   auto issue_tile = [&](int t, int stage) {
     const int k0 = kbeg + t * BN;
     uint8_t* kdst = lds + K_OFS + stage * TILE + wave_lds;
-    uint8_t* vdst = lds + V_OFS + stage * TILE + wave_lds;
+    uint8_t* vdst = lds + V_OFS + stage * TILEV + wave_lds;
     __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)k0 * row_stride), 0, tile_bytes, 0x00020000);
     __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)k0 * row_stride), 0, tile_bytes, 0x00020000);
     if (k0 + BN <= p.Nkv) {
@@ -202,7 +215,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
           so = 0;
         }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kdst + jj * WAVES * 1024), 16, ko, so, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + jj * WAVES * 1024), 16, vo, so, 0, 0);
+        if constexpr (!V8)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + jj * WAVES * 1024), 16, vo, so, 0, 0);
       }
     } else {   // last tile: rows past the end are masked; read the last valid row instead
 #pragma unroll
@@ -214,7 +228,24 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
         const uint32_t ko = (uint32_t)(((int64_t)rr * row_stride + 8 * (ld_pc ^ k_swz<SWZ>(row))) * 2);
         const uint32_t vo = (uint32_t)(((int64_t)rr * row_stride + 8 * (ld_pc ^ v_swz<RPB, VSWZ_BITS>(row))) * 2);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kdst + jj * WAVES * 1024), 16, ko, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + jj * WAVES * 1024), 16, vo, 0, 0, 0);
+        if constexpr (!V8)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + jj * WAVES * 1024), 16, vo, 0, 0, 0);
+      }
+    }
+    if constexpr (V8) {
+      // byte rows of the E4M3 V tile: instruction jj of this wave covers rows
+      // (jj*WAVES + wave)*RPIV + lane/CHV, physical chunk lane%CHV holding logical chunk
+      // (lane%CHV) ^ ((row / 2) % 8); rows past the key length read the last valid row
+      const uint32_t v8_bytes = (uint32_t)((int64_t)BN * row_stride);
+      __amdgpu_buffer_rsrc_t rv8 = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase8 + (int64_t)k0 * row_stride), 0, v8_bytes, 0x00020000);
+#pragma unroll
+      for (int jj = 0; jj < PER_WAVE_V8; ++jj) {
+        const int j = jj * WAVES + wave;
+        if (NTV % WAVES != 0 && j >= NTV) break;
+        const int row = j * RPIV + lane / CHV;
+        const int rr = (k0 + row < p.Nkv ? k0 + row : p.Nkv - 1) - k0;
+        const uint32_t vo8 = (uint32_t)((int64_t)rr * row_stride + 16 * ((lane % CHV) ^ ((row >> 1) & 7)));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv8, (__attribute__((address_space(3))) void*)(vdst + jj * WAVES * 1024), 16, vo8, 0, 0, 0);
       }
     }
     if constexpr (MASK) {
@@ -274,6 +305,20 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
     const int rl = wave * kRowsPerWave + (lane & 31);
 #pragma unroll
     for (int c = 0; c < M_CPR; ++c) maddr[c] = lds + M_OFS + rl * BN + 16 * (c ^ msw(rl)) + kl;
+  }
+  // V8: A operand of the FP8 second product (V^T: 32 rows of d x 64 keys) by byte-transposing
+  // reads (ds_read_b64_tr_b8).  Per 16-lane group G, lane i receives byte (i % 16) % 8 of the
+  // 8-byte chunks addressed by lanes 16 G + 2 j + (i % 16) / 8, j = 0..7 (measured on gfx950).
+  // Operand byte 8 c + e of lane l must be V[16 c + 8 (l / 32) + e][32 dt + l % 32] (the key order
+  // of the packed P bytes), so lane P addresses key row 16 c + 8 (G / 2) + (P % 16) / 2 at byte
+  // 32 dt + 16 (G % 2) + 8 (P % 2); the row swizzle does not depend on c.
+  const uint8_t* vaddr8[V8 ? DT : 1];
+  if constexpr (V8) {
+    const int G = lane >> 4, pp = lane & 15;
+    const int row = 8 * (G >> 1) + (pp >> 1);
+    const int sw = (row >> 1) & 7;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vaddr8[dt] = lds + V_OFS + row * D + 16 * ((2 * dt + (G & 1)) ^ sw) + 8 * (pp & 1);
   }
   const uint8_t* vaddr[DT];
   const int g = lane >> 4, li = lane & 15;
@@ -336,7 +381,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const uint8_t* a0 = vaddr[dt] + S * TILE + 16 * (2 * mt + k2) * RB;
+          const uint8_t* a0 = vaddr[dt] + S * TILEV + 16 * (2 * mt + k2) * RB;
           i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
           i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 4 * RB));
           u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
@@ -508,8 +553,90 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
         }
       }
     };
-    if (need_tail || need_causal) tile_body(std::true_type{});
-    else tile_body(std::false_type{});
+    // ---- V8: both 32-key blocks of the tile are turned into weights first (the FP8 product
+    // consumes all 64 keys at once), so the lazy-rescale test is taken per tile: exact test on
+    // the larger block maximum, or the lane's weight sum over the tile.  Weights <= 2^TAU = 256
+    // lie inside E4M3's range (448), so the round-to-nearest-even conversion never saturates.
+    auto weights8 = [&](const f32x16& sa, float mu, i32x8& pb8, int mt) {
+      float ps = 0.f;
+      float pw[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pw[r] = fast_exp2(fmaf(sa[r], c, -mu));
+        ps += pw[r];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(pw[4 * i], pw[4 * i + 1], 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(pw[4 * i + 2], pw[4 * i + 3], w, true);
+        pb8[4 * mt + i] = w;
+      }
+      return ps;
+    };
+    auto sm_start8 = [&](int mt, f32x16& sa, i32x8& pb8, auto masked_c) {
+      constexpr bool exact = decltype(masked_c)::value || MASK;
+      mask_block(mt, sa, masked_c);
+      BlockSm st{kNegInf, 0.f};
+      if constexpr (exact) st.mx = block_max(sa);
+      st.ps = weights8(sa, (m_run == kNegInf) ? 0.f : m_run, pb8, mt);
+      return st;
+    };
+    auto read_v8 = [&](int dt) {
+      typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+      i32x8 va;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vaddr8[dt] + S * TILEV + 16 * cc * D));
+        va[2 * cc] = w[0];
+        va[2 * cc + 1] = w[1];
+      }
+      return va;
+    };
+    auto tile_body8 = [&](auto masked_c) {
+      constexpr bool exact = decltype(masked_c)::value || MASK;
+      u32x4 kf[KSTEPS];
+      read_k(0, kf);
+      f32x16 s0 = qk(kf);
+      __builtin_amdgcn_sched_barrier(0);
+      read_k(1, kf);
+      f32x16 s1 = qk(kf);
+      i32x8 pb8;
+      BlockSm st0 = sm_start8(0, s0, pb8, masked_c);
+#pragma unroll
+      for (int i = 0; i < KSTEPS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+      }
+      BlockSm st1 = sm_start8(1, s1, pb8, masked_c);
+      ATTN_PIN(st0.ps);
+      ATTN_PIN(st1.ps);
+      bool raise;
+      if constexpr (exact) raise = __builtin_amdgcn_ballot_w64(fmaxf(st0.mx, st1.mx) > m_run + kTau) != 0;
+      else raise = __builtin_amdgcn_ballot_w64(st0.ps + st1.ps > kTauPow || m_run == kNegInf) != 0;
+      if (raise) {
+        const float mx = exact ? fmaxf(st0.mx, st1.mx) : fmaxf(block_max(s0), block_max(s1));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);   // 0 from empty
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
+        const float mu = (m_run == kNegInf) ? 0.f : m_run;
+        st0.ps = weights8(s0, mu, pb8, 0);
+        st1.ps = weights8(s1, mu, pb8, 1);
+      }
+      l_run += st0.ps + st1.ps;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(read_v8(dt), pb8, oacc[dt], 0, 0, 0, 0, 0, 0);
+    };
+    if constexpr (V8) {
+      if (need_tail || need_causal) tile_body8(std::true_type{});
+      else tile_body8(std::false_type{});
+    } else {
+      if (need_tail || need_causal) tile_body(std::true_type{});
+      else tile_body(std::false_type{});
+    }
   };
 #undef ATTN_PIN
 
@@ -526,7 +653,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
 
   // ---- epilogue: finish the denominator over the lane pair, normalise, store
   const float l_all = xor32_sum(l_run);
-  const float inv = l_all == 0.f ? 0.f : 1.f / l_all;
+  const float inv = l_all == 0.f ? 0.f : (V8 ? p.v_scale : 1.f) / l_all;   // V8: V's scale folded in
   const bool row_ok = qi < p.Nq;
   const int64_t rh = ((int64_t)b * p.Nq + qi) * p.H + h;   // row-head index
 
@@ -605,6 +732,21 @@ static hipError_t launch_fwd_dtype(const FwdParams& p, int D, int BN, bool split
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int BN, bool split, hipStream_t s) {
   return dtype == 0 ? launch_fwd_dtype<bf16_t>(p, D, BN, split, s) : launch_fwd_dtype<f16_t>(p, D, BN, split, s);
+}
+
+template <typename T, bool MASK>
+static hipError_t launch_fwd_v8_t(const FwdParams& p0, hipStream_t s) {
+  FwdParams p = p0;
+  p.n_qblocks = (p.Nq + 8 * kRowsPerWave - 1) / (8 * kRowsPerWave);
+  dim3 grid((unsigned)((int64_t)p.n_qblocks * p.H * p.B));
+  hipLaunchKernelGGL((attn_fwd_kernel<T, 128, 64, MASK, false, 8, 3, true>), grid, dim3(512), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8v(const FwdParams& p, int dtype, hipStream_t s) {
+  const bool mask = p.mask != nullptr;
+  if (dtype == 0) return mask ? launch_fwd_v8_t<bf16_t, true>(p, s) : launch_fwd_v8_t<bf16_t, false>(p, s);
+  return mask ? launch_fwd_v8_t<f16_t, true>(p, s) : launch_fwd_v8_t<f16_t, false>(p, s);
 }
 
 int fwd_block_m() { return kMinBlockM; }

@@ -14,7 +14,7 @@ E_NULL, E_SHAPE, E_UNSUP, E_ALIGN, E_WS = 1, 2, 3, 4, 5
 def test_library_exports_every_declared_symbol():
     names = sa.declared_symbols()
     assert {"attn_fwd", "attn_fwd_splitk", "attn_fwd_splitk_fused", "attn_combine", "attn_softmax_rows",
-            "attn_round", "attn_fwd_ex", "attn_last_error", "attn_abi_version"} <= set(names)
+            "attn_round", "attn_fwd_fp8v", "attn_fwd_ex", "attn_last_error", "attn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(sa.lib(), n), n
 
@@ -47,6 +47,10 @@ def fused(q=A, k=A, v=A, out=A, lse=None, B=1, H=1, Nq=1, Nkv=64, D=64, causal=0
 
 def softmax(x=A, y=A, rows=1, n=64, dtype=2, method=0):
     return sa.lib().attn_softmax_rows(x, y, rows, n, dtype, method, None)
+
+
+def fp8v(q=A, k=A, v=A, v_scale=1.0, out=A, lse=None, B=1, H=1, N=64, D=128, causal=0, mask=None, dtype=0):
+    return sa.lib().attn_fwd_fp8v(q, k, v, v_scale, out, lse, B, H, N, D, causal, mask, dtype, None)
 
 
 def rnd(x=A, y=A, n=64, dtype=0):
@@ -89,7 +93,17 @@ def combine(o_p=A, l_p=A, out=A, lse=None, P=4, rows=1, heads=1, depth=64, out_d
     (lambda: softmax(method=3), E_UNSUP),
     (lambda: softmax(method=1, n=4097), E_UNSUP),
     (lambda: softmax(x=A + 2), E_ALIGN),
+    (lambda: fp8v(v=None), E_NULL),
+    (lambda: fp8v(out=None), E_NULL),
+    (lambda: fp8v(D=64), E_UNSUP),
+    (lambda: fp8v(v_scale=float("inf")), E_UNSUP),
+    (lambda: fp8v(v_scale=float("nan")), E_UNSUP),
+    (lambda: fp8v(dtype=2), E_UNSUP),
+    (lambda: fp8v(v=BAD), E_ALIGN),
+    (lambda: fp8v(N=0), E_SHAPE),
     (lambda: rnd(n=-1), E_SHAPE),
+    (lambda: rnd(dtype=4), E_UNSUP),
+    (lambda: rnd(dtype=3, y=A + 1, x=A + 2), E_ALIGN),
     (lambda: rnd(x=None), E_NULL),
     (lambda: rnd(y=None), E_NULL),
     (lambda: rnd(dtype=2), E_UNSUP),
