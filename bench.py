@@ -11,8 +11,9 @@ query-key pair, causal diagonal included); the decode and combine bandwidths are
 beside it, together with a decode sweep over P in {4, 8, 16, 37} (two launches, and the same
 work fused into one attn_fwd_splitk_fused launch) and a combine measured on a workspace too large
 for the caches, the standalone row softmax (three methods) on 32768 x 4096 and 4096 x 32768
-fp32 rows, and the masked long-context prefill (B1 H16 N16384 D256, causal AND a Bernoulli(0.5)
-mask with 1/64 of the rows fully masked) beside the same shape without the mask.  Every per-kernel time comes from HIP events recorded on the
+fp32 rows, the masked long-context prefill (B1 H16 N16384 D256, causal AND a Bernoulli(0.5)
+mask with 1/64 of the rows fully masked) beside the same shape without the mask, and the prefill
+with E4M3 V on the FP8 matrix cores (attn_fwd_fp8v).  Every per-kernel time comes from HIP events recorded on the
 stream the kernels are launched on, over the whole timed region.  Rank 0 prints one JSON line.
 """
 import argparse
@@ -32,6 +33,10 @@ import seeded_inputs as si  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, published
+# attn_fwd_fp8v does half its work (Q K^T) on bf16 and half (P V) on FP8 matrix cores, so at
+# both peaks one FLOP of the mix takes (1/2)/2500 + (1/2)/5000 ps: a mixed peak of 3333 TFLOP/s
+PEAK_MIX_TFLOPS = 1.0 / (0.5 / PEAK_BF16_TFLOPS + 0.5 / PEAK_FP8_TFLOPS)
 METRIC = "attn TFLOP/s (% bf16 MFMA peak) B4 H32 N4096 D128 causal; combine GB/s"
 
 
@@ -89,6 +94,21 @@ def masked_figures(sa, dev, steps=10, warmup=3):
             "masked_TFLOP/s": fl / (m[0] * 1e-3) / 1e12, "mfma_frac": fl / (m[0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "useful_TFLOP/s": useful / (m[0] * 1e-3) / 1e12, "visible_pair_frac": vis / (s["N"] * (s["N"] + 1) / 2),
             "causal_only_ms": m[1], "causal_only_TFLOP/s": fl / (m[1] * 1e-3) / 1e12}
+
+
+def fp8v_figures(sa, dev, steps=10, warmup=3, bf16_ms=None):
+    """attn_fwd_fp8v on the prefill shape (bf16 Q/K, E4M3 V, causal)."""
+    s = si.FP8V
+    qc, kc, vc = si.fp8v_inputs()
+    q, k, v = qc.to(dev), kc.to(dev), vc.to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    fl = prefill_flops(s["B"], s["H"], s["N"], s["D"])
+    _, m = timed_events([lambda: sa.attn_fwd_fp8v(q, k, v, 1.0, out, lse, causal=True)], steps, warmup)
+    tf = fl / (m[0] * 1e-3) / 1e12
+    return {"workload": s["name"], "ms": m[0], "TFLOP/s": tf, "mixed_peak_TFLOP/s": PEAK_MIX_TFLOPS,
+            "mixed_peak_frac": tf / PEAK_MIX_TFLOPS,
+            "speedup_vs_bf16": None if bf16_ms is None else bf16_ms / m[0]}
 
 
 def combine_bytes(P, RH, D, out_elem=2):
@@ -180,7 +200,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "combine", "copy", "softmax"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "combine", "copy", "softmax", "fp8v"], default=None,
                     help="time a single kernel (for profiler runs); 'copy' times a plain 1 GiB device "
                          "copy, the calibration for the HBM byte counters")
     args = ap.parse_args()
@@ -203,6 +223,9 @@ def main():
         return
     if args.only == "softmax":
         print(json.dumps({"softmax": softmax_figures(sa, dev, args.steps, args.warmup)}), flush=True)
+        return
+    if args.only == "fp8v":
+        print(json.dumps({"fp8v_prefill": fp8v_figures(sa, dev, args.steps, args.warmup)}), flush=True)
         return
     # ---- inputs (seeded, synthetic, resident in HBM before timing) -----------------------
     sp = si.PREFILL
@@ -250,6 +273,9 @@ def main():
 
     extra = {}
     if args.only is None:
+        # ---- the prefill with E4M3 V and an FP8 second product (right after the bf16 prefill,
+        #      in the same state of the GPU) ----------------------------------------------------
+        extra["fp8v_prefill"] = fp8v_figures(sa, dev, steps=args.steps, warmup=args.warmup, bf16_ms=t.get("prefill"))
         # ---- decode sweep over P (context) -------------------------------------------------
         sweep = {}
         for P in sd["P_list"]:

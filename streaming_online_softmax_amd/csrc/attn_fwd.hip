@@ -95,7 +95,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   static_assert(WAVES == 4 || WAVES == 8, "four or eight waves per workgroup");
   static_assert(TILE % 1024 == 0, "tile must be a whole number of 1 KiB wave loads");
   // V tiles: 2 bytes per element, or 1 with V8.  V8 rows (D bytes, 8 chunks) are swizzled by
-  // chunk ^ ((row / 2) % 8), which spreads the 16 rows one byte-transposing read touches.
+  // chunk ^ (2 * ((row / 2) % 4)): the 8 rows x 2 chunks that one half-wave of a byte-transposing
+  // read touches then cover the 64 banks exactly once.
   static_assert(!V8 || (D == 128 && BN == 64 && !SPLIT), "the FP8 second product is built for D = 128, 64-key tiles");
   constexpr int RBV = V8 ? D : RB;      // bytes per V row in LDS
   constexpr int TILEV = BN * RBV;
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
     if constexpr (V8) {
       // byte rows of the E4M3 V tile: instruction jj of this wave covers rows
       // (jj*WAVES + wave)*RPIV + lane/CHV, physical chunk lane%CHV holding logical chunk
-      // (lane%CHV) ^ ((row / 2) % 8); rows past the key length read the last valid row
+      // (lane%CHV) ^ (2 * ((row / 2) % 4)); rows past the key length read the last valid row
       const uint32_t v8_bytes = (uint32_t)((int64_t)BN * row_stride);
       __amdgpu_buffer_rsrc_t rv8 = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase8 + (int64_t)k0 * row_stride), 0, v8_bytes, 0x00020000);
 #pragma unroll
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
         if (NTV % WAVES != 0 && j >= NTV) break;
         const int row = j * RPIV + lane / CHV;
         const int rr = (k0 + row < p.Nkv ? k0 + row : p.Nkv - 1) - k0;
-        const uint32_t vo8 = (uint32_t)((int64_t)rr * row_stride + 16 * ((lane % CHV) ^ ((row >> 1) & 7)));
+        const uint32_t vo8 = (uint32_t)((int64_t)rr * row_stride + 16 * ((lane % CHV) ^ (2 * ((row >> 1) & 3))));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv8, (__attribute__((address_space(3))) void*)(vdst + jj * WAVES * 1024), 16, vo8, 0, 0, 0);
       }
     }
@@ -311,12 +312,12 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   // 8-byte chunks addressed by lanes 16 G + 2 j + (i % 16) / 8, j = 0..7 (measured on gfx950).
   // Operand byte 8 c + e of lane l must be V[16 c + 8 (l / 32) + e][32 dt + l % 32] (the key order
   // of the packed P bytes), so lane P addresses key row 16 c + 8 (G / 2) + (P % 16) / 2 at byte
-  // 32 dt + 16 (G % 2) + 8 (P % 2); the row swizzle does not depend on c.
+  // 32 dt + 16 (G % 2) + 8 (P % 2); the row swizzle does not depend on c (rows move by 16 c).
   const uint8_t* vaddr8[V8 ? DT : 1];
   if constexpr (V8) {
     const int G = lane >> 4, pp = lane & 15;
     const int row = 8 * (G >> 1) + (pp >> 1);
-    const int sw = (row >> 1) & 7;
+    const int sw = 2 * ((row >> 1) & 3);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vaddr8[dt] = lds + V_OFS + row * D + 16 * ((2 * dt + (G & 1)) ^ sw) + 8 * (pp & 1);
   }
