@@ -39,14 +39,6 @@ namespace attn {
 constexpr int kRowsPerWave = 32;               // query rows (accumulator columns) per wave
 constexpr int kMinBlockM = 4 * kRowsPerWave;   // smallest query block (four waves)
 
-// Row permutation of a 32-key block inside the first product: A-operand row i holds key pi(i).
-// With it, accumulator register r of lane l holds key 16*(r/8) + 8*(l/32) + (r%8), which is
-// exactly the B-operand slot order of the second product for key step 2*mt + r/8.
-__device__ __forceinline__ int key_perm(int i) {
-  int b = i >> 3, h = (i >> 2) & 1;
-  return ((b >> 1) << 4) + (h << 3) + ((b & 1) << 2) + (i & 3);
-}
-
 // Lazy rescale threshold (log2 units): the reference maximum m is raised only when a weight
 // against the current reference could exceed 2^TAU, so weights stay <= 2^TAU and the O rescale
 // is skipped on almost every block.  O / l and m + log2(l) do not depend on which reference is

@@ -67,6 +67,15 @@ template <> struct elem<f16_t> {
   }
 };
 
+// Row permutation of a 32-key block inside the first product S^T = K Q^T: A-operand row i holds
+// key pi(i).  With it, accumulator register r of lane l holds key 16*(r/8) + 8*(l/32) + (r%8),
+// which is exactly the B-operand slot order of the second product for key step r/8, so the
+// scores convert to that operand in the lanes that hold them.
+__device__ __forceinline__ int key_perm(int i) {
+  int b = i >> 3, h = (i >> 2) & 1;
+  return ((b >> 1) << 4) + (h << 3) + ((b & 1) << 2) + (i & 3);
+}
+
 // ------------------------------------------------------------------------------------------
 // Cross-lane reductions (all 64 lanes take part; results replicated in every lane involved).
 // ------------------------------------------------------------------------------------------
