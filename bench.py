@@ -200,7 +200,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "combine", "copy", "softmax", "fp8v"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "combine", "copy", "softmax", "fp8v", "masked"], default=None,
                     help="time a single kernel (for profiler runs); 'copy' times a plain 1 GiB device "
                          "copy, the calibration for the HBM byte counters")
     args = ap.parse_args()
@@ -223,6 +223,9 @@ def main():
         return
     if args.only == "softmax":
         print(json.dumps({"softmax": softmax_figures(sa, dev, args.steps, args.warmup)}), flush=True)
+        return
+    if args.only == "masked":
+        print(json.dumps({"masked_long_context": masked_figures(sa, dev, args.steps, args.warmup)}), flush=True)
         return
     if args.only == "fp8v":
         print(json.dumps({"fp8v_prefill": fp8v_figures(sa, dev, args.steps, args.warmup)}), flush=True)

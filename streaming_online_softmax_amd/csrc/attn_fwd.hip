@@ -490,9 +490,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
     auto tile_body = [&](auto masked_c) {
       u32x4 va[2][DT];
       u32x4 pb[2];
-      // (D = 256 with a mask measured faster one block at a time: its mask reads crowd the
-      // pipelined form's registers)
-      if constexpr (MT >= 2 && (D <= 128 || !MASK)) {
+      if constexpr (MT >= 2) {
         // Software pipeline over the MT blocks of the tile: phase k issues the matrix work
         // S_{k+1} = K_{k+1} Q^T and O += V_{k-1} P_{k-1} and, on the vector ALUs meanwhile,
         // softmax(S_k), which depends on neither:
@@ -533,7 +531,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
             s_cur = s_nxt;
           }
         }
-      } else {                    // one block at a time (BN = 32; D = 256 with a mask)
+      } else {                    // one block at a time (BN = 32)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           u32x4 kfa[KSTEPS];
