@@ -103,8 +103,13 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   // LDS: [K stages | V stages].  Every operand read is a per-lane base plus a compile-time offset
   // (block, key step, stage), which must fit the 16-bit DS offset.
   constexpr int K_OFS = 0, V_OFS = NSTAGE * TILE;
-  static_assert((NSTAGE - 1) * TILE + (MT - 1) * 32 * RB < 65536, "K read offsets exceed the DS immediate");
-  static_assert((NSTAGE - 1) * TILEV + (BN - 1) * RBV < 65536, "V read offsets exceed the DS immediate");
+  constexpr int KS_PER = KSTEPS < (SWZ + 1) / 2 ? KSTEPS : (SWZ + 1) / 2;   // key steps per K swizzle group
+  constexpr int DT_PER = DT < 4 ? DT : 4;                                  // row tiles per V swizzle group
+  static_assert(VSWZ_BITS != 1 || DT <= 2, "V swizzle groups of two row tiles");
+  static_assert((NSTAGE - 1) * TILE + (MT - 1) * 32 * RB + 16 * (SWZ + 1) * ((KSTEPS - 1) / KS_PER) < 65536,
+                "K read offsets exceed the DS immediate");
+  static_assert((NSTAGE - 1) * TILEV + (BN - 1) * RBV + 64 * DT_PER * ((DT - 1) / DT_PER) < 65536,
+                "V read offsets exceed the DS immediate");
 
   constexpr int M_OFS = NSTAGE * (TILE + TILEV);
   static_assert(M_OFS + NSTAGE * MTILE <= 160 * 1024, "LDS budget of one workgroup");
@@ -284,12 +289,15 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   //      16*(2*mt + k2) + 8*(g/2) + {0..3}, {4..7}; lane 4*j + tq of the group addresses key row
   //      (.. + j), d chunk 4*tq.  Only the parts that depend on the lane are kept here; block,
   //      key step and stage are compile-time offsets.
-  const uint8_t* kaddr[KSTEPS];
+  //      The chunk swizzles only permute chunks inside aligned groups of SWZ + 1 (K) and of 16
+  //      (V, 4 row tiles), so one base per key step (row tile) of the first group serves the
+  //      later groups with an immediate offset (D = 256 needs 8 + 4 fewer address registers).
+  const uint8_t* kaddr[KS_PER];
   {
     const int krow = key_perm(lane & 31);
     const int ksw = k_swz<SWZ>(krow);
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
+    for (int ks = 0; ks < KS_PER; ++ks)
       kaddr[ks] = lds + K_OFS + krow * RB + 16 * ((2 * ks + (lane >> 5)) ^ ksw);
   }
   // mask bytes of this lane's query row: chunk c (keys 16c .. 16c+15 of the tile), half kl
@@ -313,14 +321,14 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vaddr8[dt] = lds + V_OFS + row * D + 16 * ((2 * dt + (G & 1)) ^ sw) + 8 * (pp & 1);
   }
-  const uint8_t* vaddr[DT];
+  const uint8_t* vaddr[DT_PER];
   const int g = lane >> 4, li = lane & 15;
   const bool dpad = (D < 32) && ((g & 1) != 0);    // O^T rows D..31 for D = 16: zero operand
   {
     const int jrow = li >> 2, tq = li & 3;
     const int vrow = 8 * (g >> 1) + jrow;          // the swizzle depends on the key row only through this
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int dt = 0; dt < DT_PER; ++dt) {
       const int d = 32 * dt + 16 * (g & 1) + 4 * tq;
       const int cidx = (d / 8) % CH;
       vaddr[dt] = lds + V_OFS + vrow * RB + 16 * (cidx ^ v_swz<RPB, VSWZ_BITS>(vrow)) + 8 * (tq & 1);
@@ -360,7 +368,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
     auto read_k = [&](int mt, u32x4 (&kf)[KSTEPS]) {
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks)
-        kf[ks] = *reinterpret_cast<const u32x4*>(kaddr[ks] + S * TILE + mt * 32 * RB);
+        kf[ks] = *reinterpret_cast<const u32x4*>(kaddr[ks % KS_PER] + S * TILE + mt * 32 * RB + 16 * (SWZ + 1) * (ks / KS_PER));
     };
     auto qk = [&](const u32x4 (&kf)[KSTEPS]) {
       f32x16 acc = f32x16{};
@@ -374,7 +382,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const uint8_t* a0 = vaddr[dt] + S * TILEV + 16 * (2 * mt + k2) * RB;
+          const uint8_t* a0 = vaddr[dt % DT_PER] + S * TILEV + 16 * (2 * mt + k2) * RB + 64 * DT_PER * (dt / DT_PER);
           i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
           i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 4 * RB));
           u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
