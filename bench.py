@@ -61,8 +61,6 @@ def softmax_figures(sa, dev, steps=10, warmup=3):
         nbytes = 2 * x.numel() * 4
         fig = {}
         for name, m in (("streaming", 0), ("registers", 1), ("three_pass", 2)):
-            if m == 1 and w["n"] > 4096:
-                continue
             _, ms = timed_events([lambda: sa.attn_softmax_rows(x, y, m)], steps, warmup)
             fig[name] = {"ms": ms[0], "GB/s": nbytes / (ms[0] * 1e-3) / 1e9,
                          "hbm_frac": nbytes / (ms[0] * 1e-3) / 1e9 / PEAK_HBM_GBS}

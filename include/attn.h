@@ -161,11 +161,12 @@ int attn_combine(const float* o_partial, const float* lse_partial, void* out, fl
  *   method    ATTN_SOFTMAX_STREAMING: two passes with four values per lane per step, whatever n
  *               (statistics streamed first, logits reread to write; Tylo "Streaming attention and
  *               online state", section "Online statistics");
- *             ATTN_SOFTMAX_REGISTERS: the whole row held in registers, n <= 4096, one read;
+ *             ATTN_SOFTMAX_REGISTERS: the whole row held in registers, one read: one wave per
+ *               row for n <= 4096, a 16-wave workgroup per row for 4096 < n <= 65536;
  *             ATTN_SOFTMAX_THREE_PASS: a scalar loop over max, sum of exponentials, write.
  *             All three compute the same function; they differ in memory traffic and registers.
  *   Errors: ATTN_E_NULL, ATTN_E_SHAPE (rows or n < 1, sizes overflow), ATTN_E_UNSUPPORTED (dtype,
- *   method, or n > 4096 with the registers method), ATTN_E_ALIGN.
+ *   method, or n > 65536 with the registers method), ATTN_E_ALIGN.
  */
 enum attn_softmax_method { ATTN_SOFTMAX_STREAMING = 0, ATTN_SOFTMAX_REGISTERS = 1, ATTN_SOFTMAX_THREE_PASS = 2 };
 int attn_softmax_rows(const void* x, void* y, int64_t rows, int n, int dtype, int method, void* stream);

@@ -232,6 +232,7 @@ int attn_softmax_rows(const void* x, void* y, int64_t rows, int n, int dtype, in
   if (method == ATTN_SOFTMAX_REGISTERS && n > attn::softmax_regs_max_n())
     return fail(ATTN_E_UNSUPPORTED, "the registers method holds rows of at most %d elements (got %d)", attn::softmax_regs_max_n(), n);
   if ((rows + 3) / 4 > 0x7fffffffLL || (double)rows * n > 4.0e18) return fail(ATTN_E_SHAPE, "rows * n too large");
+  if (method == ATTN_SOFTMAX_REGISTERS && n > 4096 && rows > 0x7fffffffLL) return fail(ATTN_E_SHAPE, "too many rows");
   const uintptr_t es = dtype == ATTN_FP32 ? 4 : 2;
   if (!aligned(x, es) || !aligned(y, es)) return fail(ATTN_E_ALIGN, "x and y must be aligned to their element size");
   const uintptr_t vb = 4 * es;   // four elements per vector access

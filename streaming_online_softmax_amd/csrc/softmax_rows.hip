@@ -10,7 +10,9 @@
 //           -- each lane over its own elements, merged across the wave once at the end; the
 //           second pass rereads the logits and writes the probabilities.  Registers do not grow
 //           with n.
-//   REGS    the whole row in registers (n <= 4096): one read, one write.
+//   REGS    the whole row in registers: one read, one write.  Up to 4096 elements one wave holds
+//           the row; beyond that (up to 65536) a workgroup of 16 waves holds it and the two row
+//           reductions cross the waves once each through LDS.
 //   THREE   a scalar three-pass loop (max, sum of exponentials, write), one value per lane.
 // One wave owns one row, so every reduction stays inside the wave.  Exponentials are taken in
 // base 2 of (logit - reference) * log2(e).  Rows are processed four to a workgroup (one per wave).
@@ -74,6 +76,7 @@ __device__ __forceinline__ void sm_wave_merge(float& m, float& l) {
 }
 
 constexpr int kSmRegsMax = 16;   // REGS: up to 16 steps of 4 values per lane (n <= 4096)
+constexpr int kSmWideWaves = 16; // REGS beyond 4096: 16 waves per row, up to 16 steps (n <= 65536)
 
 template <typename TE, int METHOD, bool VEC, int R>
 __global__ __launch_bounds__(256) void softmax_rows_kernel(SoftmaxParams p) {
@@ -193,10 +196,81 @@ __global__ __launch_bounds__(256) void softmax_rows_kernel(SoftmaxParams p) {
   }
 }
 
+// REGS for wide rows: one workgroup of kSmWideWaves waves per row.  Thread t holds elements
+// 4 (1024 r + t) .. +3 for r < R (16-byte accesses, consecutive threads contiguous); the row max
+// and the row sum are each reduced in the wave, then across the waves through LDS (every thread
+// folds the 16 wave values in the same order).
+template <typename TE, bool VEC, int R>
+__global__ __launch_bounds__(64 * kSmWideWaves) void softmax_rows_wide_kernel(SoftmaxParams p) {
+  using IO = sm_io<TE>;
+  constexpr int NT = 64 * kSmWideWaves;
+  __shared__ float red[2][kSmWideWaves];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int n = p.n;
+  const int64_t base = (int64_t)blockIdx.x * n;
+  f32x4 v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int j = 4 * (NT * r + t);
+    if (VEC && j + 3 < n) {
+      v[r] = IO::template load4<true>(p.x, base + j);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[r][e] = (j + e < n) ? IO::load1(p.x, base + j + e) : kNegInf;
+    }
+  }
+  float m = kNegInf;
+#pragma unroll
+  for (int r = 0; r < R; ++r) m = fmaxf(m, fmaxf(fmaxf(v[r][0], v[r][1]), fmaxf(v[r][2], v[r][3])));
+  m = across_groups_max<1>(m);
+  if (lane == 0) red[0][wave] = m;
+  __syncthreads();
+  m = red[0][0];
+#pragma unroll
+  for (int w = 1; w < kSmWideWaves; ++w) m = fmaxf(m, red[0][w]);
+  const bool empty = (m == kNegInf);
+  const float mref = empty ? 0.f : m;   // the reference (finite)
+  float l = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[r][e] = empty ? 0.f : sm_weight(v[r][e], mref);
+      l += v[r][e];
+    }
+  l = group_sum<64>(l);
+  if (lane == 0) red[1][wave] = l;
+  __syncthreads();
+  l = red[1][0];
+#pragma unroll
+  for (int w = 1; w < kSmWideWaves; ++w) l += red[1][w];
+  const float inv = empty ? 0.f : 1.f / l;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int j = 4 * (NT * r + t);
+    const f32x4 y = v[r] * inv;
+    if (VEC && j + 3 < n) {
+      IO::store4(p.y, base + j, y);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) if (j + e < n) IO::store1(p.y, base + j + e, y[e]);
+    }
+  }
+}
+
 template <typename TE, int METHOD, bool VEC>
 static hipError_t launch_sm_t(const SoftmaxParams& p, hipStream_t s) {
   dim3 grid((unsigned)((p.rows + 3) / 4));
   if constexpr (METHOD == SM_REGS) {
+    if (p.n > 256 * kSmRegsMax) {                  // a workgroup per row
+      const dim3 g2((unsigned)p.rows), b2(64 * kSmWideWaves);
+      const int wsteps = (p.n + 4 * 64 * kSmWideWaves - 1) / (4 * 64 * kSmWideWaves);
+      if (wsteps <= 2) hipLaunchKernelGGL((softmax_rows_wide_kernel<TE, VEC, 2>), g2, b2, 0, s, p);
+      else if (wsteps <= 4) hipLaunchKernelGGL((softmax_rows_wide_kernel<TE, VEC, 4>), g2, b2, 0, s, p);
+      else if (wsteps <= 8) hipLaunchKernelGGL((softmax_rows_wide_kernel<TE, VEC, 8>), g2, b2, 0, s, p);
+      else hipLaunchKernelGGL((softmax_rows_wide_kernel<TE, VEC, kSmRegsMax>), g2, b2, 0, s, p);
+      return hipGetLastError();
+    }
     const int steps = (p.n + 255) / 256;
     if (steps <= 1) hipLaunchKernelGGL((softmax_rows_kernel<TE, METHOD, VEC, 1>), grid, dim3(256), 0, s, p);
     else if (steps <= 2) hipLaunchKernelGGL((softmax_rows_kernel<TE, METHOD, VEC, 2>), grid, dim3(256), 0, s, p);
@@ -230,6 +304,6 @@ hipError_t launch_softmax_rows(const SoftmaxParams& p, int dtype, int method, bo
   return launch_sm_method<float>(p, method, vec, s);
 }
 
-int softmax_regs_max_n() { return 256 * kSmRegsMax; }
+int softmax_regs_max_n() { return 4 * 64 * kSmWideWaves * kSmRegsMax; }   // 65536
 
 }  // namespace attn

@@ -91,7 +91,7 @@ def combine(o_p=A, l_p=A, out=A, lse=None, P=4, rows=1, heads=1, depth=64, out_d
     (lambda: softmax(n=0), E_SHAPE),
     (lambda: softmax(dtype=5), E_UNSUP),
     (lambda: softmax(method=3), E_UNSUP),
-    (lambda: softmax(method=1, n=4097), E_UNSUP),
+    (lambda: softmax(method=1, n=65537), E_UNSUP),
     (lambda: softmax(x=A + 2), E_ALIGN),
     (lambda: fp8v(v=None), E_NULL),
     (lambda: fp8v(out=None), E_NULL),
