@@ -113,7 +113,7 @@ def combine_bytes(P, RH, D, out_elem=2):
     return P * RH * (D + 1) * 4 + RH * D * out_elem + RH * 4
 
 
-KERNEL_SOURCES = ("attn_fwd.hip", "device.h", "launch.h")
+KERNEL_SOURCES = ("attn_fwd_kernel.h", "attn_fwd.hip", "device.h", "launch.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_prefill_B4H32N4096D128_hbm_traffic.txt")
 
 

@@ -69,6 +69,8 @@ struct SoftmaxParams {
 };
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int BN, bool split, hipStream_t s);
+// D = 256 instantiations (attn_fwd_d256.hip), called by launch_fwd
+hipError_t launch_fwd_d256(const FwdParams& p, int dtype, bool split, hipStream_t s);
 // D = 128, E4M3 V, FP8 second product (p.P = 1)
 hipError_t launch_fwd_fp8v(const FwdParams& p, int dtype, hipStream_t s);
 hipError_t launch_softmax_rows(const SoftmaxParams& p, int dtype, int method, bool vec, hipStream_t s);
