@@ -12,14 +12,17 @@ beside it, together with a decode sweep over P in {4, 8, 16, 37} (two launches, 
 work fused into one attn_fwd_splitk_fused launch) and a combine measured on a workspace too large
 for the caches, the standalone row softmax (three methods) on 32768 x 4096 and 4096 x 32768
 fp32 rows, the masked long-context prefill (B1 H16 N16384 D256, causal AND a Bernoulli(0.5)
-mask with 1/64 of the rows fully masked) beside the same shape without the mask, and the prefill
-with E4M3 V on the FP8 matrix cores (attn_fwd_fp8v).  Every per-kernel time comes from HIP events recorded on the
+mask with 1/64 of the rows fully masked) beside the same shape without the mask, the prefill
+with E4M3 V on the FP8 matrix cores (attn_fwd_fp8v), the decode-shape combine on cold workspaces
+(cycling through more than 1 GiB of them), 32- vs 64-key tiles on a single-head N2048 D64 shape,
+and the shader clock rocm-smi reports right after the timed region.  Every per-kernel time comes from HIP events recorded on the
 stream the kernels are launched on, over the whole timed region.  Rank 0 prints one JSON line.
 """
 import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -107,6 +110,63 @@ def fp8v_figures(sa, dev, steps=10, warmup=3, bf16_ms=None):
     return {"workload": s["name"], "ms": m[0], "TFLOP/s": tf, "mixed_peak_TFLOP/s": PEAK_MIX_TFLOPS,
             "mixed_peak_frac": tf / PEAK_MIX_TFLOPS,
             "speedup_vs_bf16": None if bf16_ms is None else bf16_ms / m[0]}
+
+
+def combine_cold_figures(sa, dev, sd):
+    """attn_combine at the decode shape (rows B*Nq, heads H, depth D) for each P of the sweep,
+    each call on a different workspace of a set larger than 1 GiB."""
+    res = {}
+    RH = sd["B"] * sd["H"]
+    for P in sd["P_list"]:
+        one = P * RH * (sd["D"] + 1) * 4
+        copies = max(8, (1 << 30) // one + 1)
+        op = torch.randn((copies, P, sd["B"], sd["H"], sd["D"]), dtype=torch.float32, device=dev)
+        lp = torch.randn((copies, P, sd["B"], sd["H"]), dtype=torch.float32, device=dev)
+        ob = torch.empty((sd["B"], sd["H"], sd["D"]), dtype=torch.bfloat16, device=dev)
+        for c in range(min(copies, 16)):
+            sa.attn_combine(op[c], lp[c], ob)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for c in range(copies):
+            sa.attn_combine(op[c], lp[c], ob)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / copies
+        cb = combine_bytes(P, RH, sd["D"])
+        res[str(P)] = {"copies": copies, "us": ms * 1e3, "GB/s": cb / (ms * 1e-3) / 1e9}
+        del op, lp
+    return res
+
+
+def block_n_figures(sa, dev, steps=20, warmup=5):
+    """Single-head attn_fwd, N 2048, D 64, bf16, causal and not: 32- vs 64-key tiles (context;
+    launch-latency-sized work)."""
+    q, k, v = (t.to(dev) for t in si.prefill_inputs(B=1, H=1, N=2048))
+    q, k, v = (t[..., :64].contiguous() for t in (q, k, v))
+    res = {}
+    for causal in (False, True):
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        _, m = timed_events([lambda: sa.attn_fwd(q, k, v, out, lse, causal=causal, block_n=32),
+                             lambda: sa.attn_fwd(q, k, v, out, lse, causal=causal, block_n=64)], steps, warmup)
+        res["causal" if causal else "full"] = {"BN32_us": m[0] * 1e3, "BN64_us": m[1] * 1e3}
+    return res
+
+
+def gpu_clock():
+    """Shader clock reported by rocm-smi right after the timed region (None if unavailable)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], stdout=subprocess.PIPE, stderr=subprocess.DEVNULL,
+                           text=True, timeout=20)
+        for line in r.stdout.splitlines():
+            if "sclk" in line:
+                mhz = re.search(r"\((\d+)\s*Mhz\)", line, re.IGNORECASE)
+                return f"{mhz.group(1)} MHz" if mhz else line.strip()
+    except (OSError, subprocess.SubprocessError):
+        return None
+    return None
 
 
 def combine_bytes(P, RH, D, out_elem=2):
@@ -258,6 +318,7 @@ def main():
         args.only, [k_prefill, k_decode, k_combine])
     torch.cuda.synchronize()
     wall, ms = timed_events(fns, args.steps, args.warmup)
+    clock = gpu_clock()
     assert not torch.isnan(out).any() and not torch.isnan(dout).any(), "NaN in outputs"
 
     names = {"prefill": ["prefill"], "decode": ["decode"], "combine": ["decode", "combine"]}.get(
@@ -293,8 +354,12 @@ def main():
             _, mf = timed_events([lambda: sa.attn_fwd_splitk_fused(dq, dk, dv, P, op, lp, tk, ob, fl_)], 10, 3)
             fb = decode_bytes(sd["B"], sd["H"], sd["Nkv"], sd["D"], P) + combine_bytes(P, RH, sd["D"])
             sweep[str(P)].update({"fused_ms": mf[0], "fused_GB/s": fb / (mf[0] * 1e-3) / 1e9,
-                                  "two_launch_ms": m[0] + m[1]})
+                                  "two_launch_ms": m[0] + m[1],
+                                  "pipeline_GB/s": fb / ((m[0] + m[1]) * 1e-3) / 1e9})
         extra["decode_sweep"] = sweep
+        # ---- the combine at the decode shape with its workspace cold: cycle through enough
+        #      separate workspaces (> 1 GiB) that each call reads from HBM, not the caches
+        extra["combine_cold"] = combine_cold_figures(sa, dev, sd)
         # ---- combine on a workspace larger than the caches (rows 8192, heads 32, depth 128) -
         Pc, rows_c = 16, 8192
         opc = torch.randn((Pc, rows_c, sd["H"], sd["D"]), dtype=torch.float32, device=dev)
@@ -306,6 +371,8 @@ def main():
                                   "GB/s": cb / (m[0] * 1e-3) / 1e9,
                                   "hbm_frac": cb / (m[0] * 1e-3) / 1e9 / PEAK_HBM_GBS}
         del opc, lpc, obc
+        # ---- single-head shape, 32- vs 64-key tiles (context) --------------------------------
+        extra["block_n_single_head_N2048_D64"] = block_n_figures(sa, dev)
         # ---- standalone row softmax (32768 rows x 4096 fp32; and 4096 x 32768) -------------
         extra["softmax"] = softmax_figures(sa, dev)
         # ---- masked long context B1 H16 N16384 D256, causal AND Bernoulli(0.5) mask ----------
@@ -329,6 +396,7 @@ def main():
                    "step": "attn_fwd(prefill) + attn_fwd_splitk(decode B8 H32 Nq1 Nkv32768 D128 bf16, P=16) + attn_combine",
                    "B": sp["B"], "H": sp["H"], "N": sp["N"], "D": sp["D"], "causal": True},
         "kernel_ms": t,
+        "gpu_clock_after_timing": clock,
         "roofline": None,
         "decode": None if "decode" not in t else {
             "GB/s": res["decode_gbs"], "hbm_frac": res["decode_gbs"] / PEAK_HBM_GBS, "P": P_STEP},
