@@ -20,7 +20,8 @@
  *   attn_softmax_rows        standalone row softmax (streaming, registers or three-pass)
  *                    with the all-masked conventions of Tylo.jl "Register fragments and
  *                    logical axes", section "Worked softmax".
- *   attn_fwd_fp8v    attn_fwd with V as E4M3 and P rounded to E4M3 for the FP8 matrix cores.
+ *   attn_fwd_fp8v    attn_fwd with V as E4M3 or E5M2 and P rounded to E4M3 for the FP8
+ *                    matrix cores.
  *   attn_round       FP32 -> bf16 / fp16 / E4M3 with the conversion the kernels apply to the
  *                    probabilities and to the output (exposed so it can be checked bit by bit).
  *
@@ -64,7 +65,8 @@ enum attn_dtype {
   ATTN_BF16 = 0,
   ATTN_FP16 = 1,
   ATTN_FP32 = 2,     /* combine / softmax only */
-  ATTN_FP8_E4M3 = 3  /* V of attn_fwd_fp8v; attn_round target */
+  ATTN_FP8_E4M3 = 3, /* V of attn_fwd_fp8v; attn_round target */
+  ATTN_FP8_E5M2 = 4  /* V of attn_fwd_fp8v */
 };
 
 enum attn_status {
@@ -206,22 +208,26 @@ int attn_fwd_ex(const struct attn_fwd_args* a, void* stream);
 /*
  * attn_fwd_fp8v -- attn_fwd with V in 8-bit floating point and the second product (P.V) on the
  *   FP8 matrix cores.  Element types from Tylo.jl "Register fragments and logical axes", section
- *   "Logical types and register packing" (Float8E4M3: four 8-bit values per 32-bit register;
- *   FP32 conversion to nearest even, saturating to the largest finite value); the recurrence is
- *   attn_fwd's.  The value of V[b, j, h, d] is decode_E4M3(v[b, j, h, d]) * v_scale.  Each
+ *   "Logical types and register packing" (Float8E4M3 and Float8E5M2: four 8-bit values per
+ *   32-bit register; FP32 conversion to nearest even, saturating to the largest finite value);
+ *   the recurrence is attn_fwd's.  The value of V[b, j, h, d] is decode(v[b, j, h, d]) * v_scale
+ *   in the format v_format names.  Each
  *   probability is rounded from FP32 to E4M3 (nearest even; it is at most 256, inside E4M3's
  *   range) before the product, while the denominator l keeps the unrounded FP32 weights (the
  *   rounding-before-PV rule of Tylo.jl "Streaming attention and online state", section
  *   "Attention as a consumer").  Q K^T stays in q/k's type.
  *   q, k, out  [B, N, H, D] bf16 or fp16 (dtype), 16-byte aligned; D must be 128.
- *   v          [B, N, H, D] E4M3 codes, one byte per element (S.EEEE.MMM, bias 7, no
- *              infinities, S.1111.111 = NaN), 16-byte aligned; codes must be finite.
+ *   v          [B, N, H, D] 8-bit codes, one byte per element, 16-byte aligned; codes must be
+ *              finite.
+ *   v_format   ATTN_FP8_E4M3 (S.EEEE.MMM, bias 7, no infinities, S.1111.111 = NaN) or
+ *              ATTN_FP8_E5M2 (S.EEEEE.MM, bias 15, IEEE-like).
  *   v_scale    finite FP32 scale of V (1.0 when V is stored unscaled).
  *   lse, causal, mask, stream: as attn_fwd (lse is the LSE of the scores, unaffected by v_scale).
- *   Errors: those of attn_fwd; ATTN_E_UNSUPPORTED also for D != 128 or a non-finite v_scale.
+ *   Errors: those of attn_fwd; ATTN_E_UNSUPPORTED also for D != 128, another v_format or a
+ *   non-finite v_scale.
  */
-int attn_fwd_fp8v(const void* q, const void* k, const uint8_t* v, float v_scale, void* out, float* lse, int B,
-                  int H, int N, int D, int causal, const uint8_t* mask, int dtype, void* stream);
+int attn_fwd_fp8v(const void* q, const void* k, const uint8_t* v, int v_format, float v_scale, void* out,
+                  float* lse, int B, int H, int N, int D, int causal, const uint8_t* mask, int dtype, void* stream);
 
 /* Message describing the calling thread's last non-OK return ("" if none). */
 const char* attn_last_error(void);

@@ -252,13 +252,13 @@ def round_fp8_bits(x, target):
     return out
 
 
-def attn_dense_fp8v(q, k, v_codes, v_scale, causal=False, mask=None, rows=None):
-    """O1 with V given as E4M3 codes and a scale: the values the kernel consumes are
-    decode(v_codes) * v_scale (exact in float64); q and k (bf16 / f16) widen exactly."""
+def attn_dense_fp8v(q, k, v_codes, v_scale, causal=False, mask=None, rows=None, v_format="e4m3"):
+    """O1 with V given as 8-bit codes (E4M3 or E5M2) and a scale: the values the kernel consumes
+    are decode(v_codes) * v_scale (exact in float64); q and k (bf16 / f16) widen exactly."""
     qd = _as_cpu_tensor(q).to(torch.float64)
     kd = _as_cpu_tensor(k).to(torch.float64)
     codes = v_codes.cpu().numpy() if isinstance(v_codes, torch.Tensor) else np.asarray(v_codes)
-    vd = torch.from_numpy(decode_bits(codes, "e4m3") * float(v_scale))
+    vd = torch.from_numpy(decode_bits(codes, v_format) * float(v_scale))
     return attn_dense(qd, kd, vd, causal=causal, mask=mask, rows=rows)
 
 

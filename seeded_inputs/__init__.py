@@ -83,13 +83,21 @@ def cast_e4m3(x):
     return t.to(torch.float8_e4m3fn).view(torch.uint8)
 
 
-def fp8v_inputs(B=None, H=None, N=None, case=0, dtype="bf16"):
-    """q, k in dtype and v as E4M3 codes, all [B, N, H, D], drawn like the prefill workload."""
+def cast_e5m2(x):
+    """float32 numpy -> uint8 torch CPU tensor of E5M2 codes (torch's float8_e5m2 conversion,
+    round to nearest even)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e5m2).view(torch.uint8)
+
+
+def fp8v_inputs(B=None, H=None, N=None, case=0, dtype="bf16", v_format="e4m3"):
+    """q, k in dtype and v as 8-bit codes (E4M3 or E5M2), all [B, N, H, D], drawn like the
+    prefill workload."""
     s = FP8V
     B, H, N = B or s["B"], H or s["H"], N or s["N"]
     rng = rng_for(CFG_FP8V, case)
     q, k, v = draw_qkv(rng, (B, N, H, s["D"]), (B, N, H, s["D"]))
-    return cast(q, dtype), cast(k, dtype), cast_e4m3(v)
+    return cast(q, dtype), cast(k, dtype), (cast_e4m3(v) if v_format == "e4m3" else cast_e5m2(v))
 
 
 def bernoulli_mask(rng, Nq, Nkv, n_full_rows, row_block=1024):

@@ -12,7 +12,7 @@ Entry points (same names as the C ABI in include/attn.h):
                           mask=None, stream=None)
     attn_combine(o_partial, lse_partial, out, lse_out=None, stream=None)
     attn_softmax_rows(x, y, method=SOFTMAX_STREAMING, stream=None)   (x, y: [..., n])
-    attn_fwd_fp8v(q, k, v, v_scale, out, lse=None, causal=False, mask=None, stream=None)
+    attn_fwd_fp8v(q, k, v, v_scale, out, lse=None, causal=False, mask=None, v_format=None, stream=None)
     attn_round(x, y, stream=None)    (x float32, y bf16/fp16/E4M3, same number of elements)
     attn_last_error(), attn_abi_version()
 Tensors are torch tensors on the GPU, contiguous, laid out as the header states
@@ -30,7 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "attn.h")
 
-ATTN_BF16, ATTN_FP16, ATTN_FP32, ATTN_FP8_E4M3 = 0, 1, 2, 3
+ATTN_BF16, ATTN_FP16, ATTN_FP32, ATTN_FP8_E4M3, ATTN_FP8_E5M2 = 0, 1, 2, 3, 4
 STATUS = {0: "ATTN_OK", 1: "ATTN_E_NULL", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUPPORTED",
           4: "ATTN_E_ALIGN", 5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
 P_MAX = 256
@@ -75,7 +75,7 @@ def _load():
     L.attn_softmax_rows.argtypes = [vp, vp, ctypes.c_int64, i32, i32, i32, vp]
     L.attn_softmax_rows.restype = i32
     L.attn_round.argtypes = [vp, vp, ctypes.c_int64, i32, vp]
-    L.attn_fwd_fp8v.argtypes = [vp, vp, vp, ctypes.c_float, vp, vp, i32, i32, i32, i32, i32, vp, i32, vp]
+    L.attn_fwd_fp8v.argtypes = [vp, vp, vp, i32, ctypes.c_float, vp, vp, i32, i32, i32, i32, i32, vp, i32, vp]
     L.attn_fwd_fp8v.restype = i32
     L.attn_round.restype = i32
     L.attn_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
@@ -171,10 +171,14 @@ def attn_softmax_rows(x, y, method=SOFTMAX_STREAMING, stream=None):
     _check(lib().attn_softmax_rows(_ptr(x), _ptr(y), rows, n, _dtype_code(x), int(method), _stream(stream)))
 
 
-def _fp8_code(t):
-    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+def _fp8_code(t, fmt=None):
+    """Format code of 8-bit data: float8_e4m3fn / float8_e5m2 tensors name their format; uint8
+    codes take `fmt` ('e4m3' unless given)."""
+    if t.dtype == torch.float8_e4m3fn or (t.dtype == torch.uint8 and fmt in (None, "e4m3")):
         return ATTN_FP8_E4M3
-    raise AttnError(3, f"E4M3 data must be uint8 codes or torch.float8_e4m3fn (got {t.dtype})")
+    if t.dtype == torch.float8_e5m2 or (t.dtype == torch.uint8 and fmt == "e5m2"):
+        return ATTN_FP8_E5M2
+    raise AttnError(3, f"8-bit data must be uint8 codes, float8_e4m3fn or float8_e5m2 (got {t.dtype}, {fmt})")
 
 
 def attn_round(x, y, stream=None):
@@ -186,14 +190,15 @@ def attn_round(x, y, stream=None):
     _check(lib().attn_round(_ptr(x), _ptr(y), x.numel(), code, _stream(stream)))
 
 
-def attn_fwd_fp8v(q, k, v, v_scale, out, lse=None, causal=False, mask=None, stream=None):
-    """attn_fwd with V as E4M3 codes (uint8 or float8_e4m3fn, [B, N, H, D]) of value code * v_scale;
-    P is rounded to E4M3 for the FP8 second product.  D must be 128."""
+def attn_fwd_fp8v(q, k, v, v_scale, out, lse=None, causal=False, mask=None, v_format=None, stream=None):
+    """attn_fwd with V as 8-bit codes ([B, N, H, D]: float8_e4m3fn, float8_e5m2, or uint8 with
+    v_format 'e4m3' / 'e5m2') of value decode(code) * v_scale; P is rounded to E4M3 for the FP8
+    second product.  D must be 128."""
     B, N, H, D = q.shape
-    _fp8_code(v)
+    fmt = _fp8_code(v, v_format)
     if tuple(v.shape) != (B, N, H, D):
         raise AttnError(2, f"v must be [B, N, H, D] = {(B, N, H, D)} (got {tuple(v.shape)})")
-    _check(lib().attn_fwd_fp8v(_ptr(q), _ptr(k), _ptr(v), float(v_scale), _ptr(out), _ptr(lse), B, H, N, D,
+    _check(lib().attn_fwd_fp8v(_ptr(q), _ptr(k), _ptr(v), fmt, float(v_scale), _ptr(out), _ptr(lse), B, H, N, D,
                                int(bool(causal)), _ptr(mask), _dtype_code(q), _stream(stream)))
 
 
@@ -205,10 +210,10 @@ def fwd(q, k, v, causal=False, mask=None, block_n=0, with_lse=True):
     return out, lse
 
 
-def fwd_fp8v(q, k, v, v_scale=1.0, causal=False, mask=None):
+def fwd_fp8v(q, k, v, v_scale=1.0, causal=False, mask=None, v_format=None):
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    attn_fwd_fp8v(q, k, v, v_scale, out, lse, causal=causal, mask=mask)
+    attn_fwd_fp8v(q, k, v, v_scale, out, lse, causal=causal, mask=mask, v_format=v_format)
     return out, lse
 
 

@@ -133,11 +133,13 @@ int attn_fwd_ex(const struct attn_fwd_args* a, void* stream) {
   return fwd_impl(a, (hipStream_t)stream);
 }
 
-int attn_fwd_fp8v(const void* q, const void* k, const uint8_t* v, float v_scale, void* out, float* lse, int B,
-                  int H, int N, int D, int causal, const uint8_t* mask, int dtype, void* stream) {
+int attn_fwd_fp8v(const void* q, const void* k, const uint8_t* v, int v_format, float v_scale, void* out,
+                  float* lse, int B, int H, int N, int D, int causal, const uint8_t* mask, int dtype, void* stream) {
   int rc = check_qkv(q, k, v, B, H, N, N, D, causal, dtype);
   if (rc) return rc;
   if (D != 128) return fail(ATTN_E_UNSUPPORTED, "attn_fwd_fp8v is built for D = 128 (got %d)", D);
+  if (v_format != ATTN_FP8_E4M3 && v_format != ATTN_FP8_E5M2)
+    return fail(ATTN_E_UNSUPPORTED, "v_format %d not supported (ATTN_FP8_E4M3 or ATTN_FP8_E5M2)", v_format);
   if (!std::isfinite(v_scale)) return fail(ATTN_E_UNSUPPORTED, "v_scale must be finite");
   if (!out) return fail(ATTN_E_NULL, "out must be a non-NULL device pointer");
   if (!aligned(out, 16)) return fail(ATTN_E_ALIGN, "out must be 16-byte aligned");
@@ -155,7 +157,8 @@ int attn_fwd_fp8v(const void* q, const void* k, const uint8_t* v, float v_scale,
   p.mask_lds = mask && aligned(mask, 16) && (N % 16 == 0) && ((int64_t)N + 256) * N < (1LL << 32);
   p.scale_log2 = scale_log2(D);
   p.v_scale = v_scale;
-  return hip_status(attn::launch_fwd_fp8v(p, dtype, (hipStream_t)stream), "attn_fwd_fp8v launch");
+  return hip_status(attn::launch_fwd_fp8v(p, dtype, v_format == ATTN_FP8_E5M2 ? 1 : 0, (hipStream_t)stream),
+                    "attn_fwd_fp8v launch");
 }
 
 int attn_fwd_splitk(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,

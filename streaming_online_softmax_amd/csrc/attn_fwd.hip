@@ -20,19 +20,23 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int BN, bool split, 
   return dtype == 0 ? launch_fwd_dtype<bf16_t>(p, D, BN, split, s) : launch_fwd_dtype<f16_t>(p, D, BN, split, s);
 }
 
-template <typename T, bool MASK>
+template <typename T, bool MASK, int FMT>
 static hipError_t launch_fwd_v8_t(const FwdParams& p0, hipStream_t s) {
   FwdParams p = p0;
   p.n_qblocks = (p.Nq + 8 * kRowsPerWave - 1) / (8 * kRowsPerWave);
   dim3 grid((unsigned)((int64_t)p.n_qblocks * p.H * p.B));
-  hipLaunchKernelGGL((attn_fwd_kernel<T, 128, 64, MASK, false, 8, 3, true>), grid, dim3(512), 0, s, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, 128, 64, MASK, false, 8, 3, FMT>), grid, dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_fp8v(const FwdParams& p, int dtype, hipStream_t s) {
-  const bool mask = p.mask != nullptr;
-  if (dtype == 0) return mask ? launch_fwd_v8_t<bf16_t, true>(p, s) : launch_fwd_v8_t<bf16_t, false>(p, s);
-  return mask ? launch_fwd_v8_t<f16_t, true>(p, s) : launch_fwd_v8_t<f16_t, false>(p, s);
+template <typename T, int FMT>
+static hipError_t launch_fwd_v8_mask(const FwdParams& p, hipStream_t s) {
+  return p.mask != nullptr ? launch_fwd_v8_t<T, true, FMT>(p, s) : launch_fwd_v8_t<T, false, FMT>(p, s);
+}
+
+hipError_t launch_fwd_fp8v(const FwdParams& p, int dtype, int v_format, hipStream_t s) {
+  if (dtype == 0) return v_format == 1 ? launch_fwd_v8_mask<bf16_t, 2>(p, s) : launch_fwd_v8_mask<bf16_t, 1>(p, s);
+  return v_format == 1 ? launch_fwd_v8_mask<f16_t, 2>(p, s) : launch_fwd_v8_mask<f16_t, 1>(p, s);
 }
 
 int fwd_block_m() { return kMinBlockM; }

@@ -58,9 +58,10 @@ __device__ __forceinline__ int v_swz(int row) { return BITS ? 4 * ((row / RPB) &
 template <int S> using stage_t = std::integral_constant<int, S>;
 
 // WAVES waves of 32 query rows each; BN keys per tile.
-// V8: V is E4M3 (one byte per element) and the second product runs on the FP8 matrix cores
-// (v_mfma_f32_32x32x64_f8f6f4, one 64-key tile per instruction), with P rounded to E4M3.
-template <typename T, int D, int BN, bool MASK, bool SPLIT, int WAVES, int NSTAGES, bool V8 = false>
+// V8: 0 = V in T; 1 / 2 = V in E4M3 / E5M2 (one byte per element) and the second product on the
+// FP8 matrix cores (v_mfma_f32_32x32x64_f8f6f4, one 64-key tile per instruction) with P rounded
+// to E4M3.
+template <typename T, int D, int BN, bool MASK, bool SPLIT, int WAVES, int NSTAGES, int V8 = 0>
 __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void attn_fwd_kernel(FwdParams p) {
   using E = elem<T>;
   constexpr int kBlockM = WAVES * kRowsPerWave;
@@ -630,7 +631,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
       l_run += st0.ps + st1.ps;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(read_v8(dt), pb8, oacc[dt], 0, 0, 0, 0, 0, 0);
+        // operand formats: A (V^T) E4M3 (0) or E5M2 (1), B (P) E4M3 (0)
+        oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(read_v8(dt), pb8, oacc[dt], V8 == 2 ? 1 : 0, 0, 0, 0, 0, 0);
     };
     if constexpr (V8) {
       if (need_tail || need_causal) tile_body8(std::true_type{});

@@ -26,7 +26,7 @@ struct FwdParams {
   int mask_lds;         // mask tiles may be staged into LDS 16 bytes at a time (row starts
                         // 16-byte aligned, (Nq + 256) * Nkv < 2^32)
   float scale_log2;     // log2(e) / sqrt(D)
-  float v_scale;        // E4M3 V (attn_fwd_fp8v): value = decoded code * v_scale
+  float v_scale;        // 8-bit V (attn_fwd_fp8v): value = decoded code * v_scale
 };
 
 // Bandwidth-bound split-K decode producer (one workgroup per row-head and partition).
@@ -71,8 +71,8 @@ struct SoftmaxParams {
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int BN, bool split, hipStream_t s);
 // D = 256 instantiations (attn_fwd_d256.hip), called by launch_fwd
 hipError_t launch_fwd_d256(const FwdParams& p, int dtype, bool split, hipStream_t s);
-// D = 128, E4M3 V, FP8 second product (p.P = 1)
-hipError_t launch_fwd_fp8v(const FwdParams& p, int dtype, hipStream_t s);
+// D = 128, 8-bit V (v_format 0 = E4M3, 1 = E5M2), FP8 second product (p.P = 1)
+hipError_t launch_fwd_fp8v(const FwdParams& p, int dtype, int v_format, hipStream_t s);
 hipError_t launch_softmax_rows(const SoftmaxParams& p, int dtype, int method, bool vec, hipStream_t s);
 int softmax_regs_max_n();
 // FP32 -> bf16 (dtype 0), fp16 (dtype 1) or E4M3 (dtype 3, saturating), n values, with the

@@ -49,8 +49,9 @@ def softmax(x=A, y=A, rows=1, n=64, dtype=2, method=0):
     return sa.lib().attn_softmax_rows(x, y, rows, n, dtype, method, None)
 
 
-def fp8v(q=A, k=A, v=A, v_scale=1.0, out=A, lse=None, B=1, H=1, N=64, D=128, causal=0, mask=None, dtype=0):
-    return sa.lib().attn_fwd_fp8v(q, k, v, v_scale, out, lse, B, H, N, D, causal, mask, dtype, None)
+def fp8v(q=A, k=A, v=A, v_format=3, v_scale=1.0, out=A, lse=None, B=1, H=1, N=64, D=128, causal=0, mask=None,
+         dtype=0):
+    return sa.lib().attn_fwd_fp8v(q, k, v, v_format, v_scale, out, lse, B, H, N, D, causal, mask, dtype, None)
 
 
 def rnd(x=A, y=A, n=64, dtype=0):
@@ -101,6 +102,8 @@ def combine(o_p=A, l_p=A, out=A, lse=None, P=4, rows=1, heads=1, depth=64, out_d
     (lambda: fp8v(dtype=2), E_UNSUP),
     (lambda: fp8v(v=BAD), E_ALIGN),
     (lambda: fp8v(N=0), E_SHAPE),
+    (lambda: fp8v(v_format=0), E_UNSUP),
+    (lambda: fp8v(v_format=5), E_UNSUP),
     (lambda: rnd(n=-1), E_SHAPE),
     (lambda: rnd(dtype=4), E_UNSUP),
     (lambda: rnd(dtype=3, y=A + 1, x=A + 2), E_ALIGN),

@@ -1,5 +1,5 @@
-"""attn_fwd_fp8v (E4M3 V, probabilities rounded to E4M3 for the FP8 matrix cores) and the E4M3
-conversion, through the C ABI, against the oracle (O1 with V decoded exactly, O6).
+"""attn_fwd_fp8v (E4M3 or E5M2 V, probabilities rounded to E4M3 for the FP8 matrix cores) and the
+E4M3 conversion, through the C ABI, against the oracle (O1 with V decoded exactly, O6).
 
 Tolerance, per output element, derived from the arithmetic (the pages give none for 8-bit
 operands).  With w_j = exp(s_j - M) the exact weights of row i (M its maximum, L = sum w_j) and
@@ -35,11 +35,11 @@ def sa():
     return mod
 
 
-def _bound(q, k, v_codes, v_scale, causal, mask, rows, ref, dtype):
+def _bound(q, k, v_codes, v_scale, causal, mask, rows, ref, dtype, v_format="e4m3"):
     """Per-element bound for the selected row-heads rh = (b*N + i)*H + h."""
     qd = q.double().numpy()
     kd = k.double().numpy()
-    vd = oracle.decode_bits(v_codes.numpy(), "e4m3") * v_scale
+    vd = oracle.decode_bits(v_codes.numpy(), v_format) * v_scale
     B, N, H, D = qd.shape
     u_out = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
     rows = np.asarray(rows)
@@ -67,19 +67,19 @@ def _bound(q, k, v_codes, v_scale, causal, mask, rows, ref, dtype):
     return out + u_out * np.abs(ref) + 2.0 ** -20
 
 
-def _check(sa, q, k, v, v_scale, causal, mask, dtype, rows=None, what=""):
+def _check(sa, q, k, v, v_scale, causal, mask, dtype, rows=None, what="", v_format="e4m3"):
     B, N, H, D = q.shape
     md = None if mask is None else torch.from_numpy(mask).to(DEV)
-    out, lse = sa.fwd_fp8v(q.to(DEV), k.to(DEV), v.to(DEV), v_scale, causal=causal, mask=md)
+    out, lse = sa.fwd_fp8v(q.to(DEV), k.to(DEV), v.to(DEV), v_scale, causal=causal, mask=md, v_format=v_format)
     torch.cuda.synchronize()
     if rows is None:
         rows = np.arange(B * N * H)
-    ref, ref_lse = oracle.attn_dense_fp8v(q, k, v, v_scale, causal=causal, mask=mask, rows=rows)
+    ref, ref_lse = oracle.attn_dense_fp8v(q, k, v, v_scale, causal=causal, mask=mask, rows=rows, v_format=v_format)
     rt = torch.from_numpy(np.asarray(rows)).to(DEV)
     o = out.reshape(-1, D)[rt].float().cpu().numpy().astype(np.float64)
     l = lse.reshape(-1)[rt].cpu().numpy().astype(np.float64)
     assert not np.isnan(o).any(), f"{what}: NaN"
-    bnd = _bound(q, k, v, v_scale, causal, mask, rows, ref, dtype)
+    bnd = _bound(q, k, v, v_scale, causal, mask, rows, ref, dtype, v_format)
     excess = np.abs(o - ref) - bnd
     worst = np.unravel_index(np.argmax(excess), excess.shape)
     assert excess.max() <= 0, (f"{what}: |dO| {abs(o - ref)[worst]:.3e} > bound {bnd[worst]:.3e} at {worst}; "
@@ -112,6 +112,23 @@ def test_fp8v_against_oracle(sa, N, causal, masked, dtype, scale):
     if masked:
         mask, _ = si.bernoulli_mask(si.rng_for(si.CFG_FP8V, 100 + case), N, N, max(1, N // 64))
     _check(sa, q, k, v, scale, causal, mask, dtype, what=f"N={N} causal={causal} mask={masked} {dtype}")
+
+
+E5M2_CASES = [(N, causal, masked, dtype) for N in (17, 200, 1000) for causal in (False, True)
+              for masked in (False, True) for dtype in ("bf16", "f16")]
+
+
+@pytest.mark.parametrize("N,causal,masked,dtype", E5M2_CASES,
+                         ids=[f"N{n}-{'c' if c else 'nc'}-{'m' if m else 'nm'}-{d}" for n, c, m, d in E5M2_CASES])
+def test_fp8v_e5m2_against_oracle(sa, N, causal, masked, dtype):
+    """V as E5M2 codes (the FP8 instruction's A operand in its E5M2 form; P stays E4M3)."""
+    case = 200 + E5M2_CASES.index((N, causal, masked, dtype))
+    q, k, v = si.fp8v_inputs(B=2, H=2, N=N, case=case, dtype=dtype, v_format="e5m2")
+    mask = None
+    if masked:
+        mask, _ = si.bernoulli_mask(si.rng_for(si.CFG_FP8V, 100 + case), N, N, max(1, N // 64))
+    _check(sa, q, k, v, 0.5, causal, mask, dtype, what=f"e5m2 N={N} causal={causal} mask={masked} {dtype}",
+           v_format="e5m2")
 
 
 def test_fp8v_single_key_and_uniform(sa):
@@ -173,4 +190,6 @@ def test_fp8v_rejects(sa):
     with pytest.raises(sa.AttnError):
         sa.fwd_fp8v(q, q, v, float("inf"))
     with pytest.raises(sa.AttnError):
-        sa.fwd_fp8v(q, q, v.view(torch.int8), 1.0)   # not E4M3 codes
+        sa.fwd_fp8v(q, q, v.view(torch.int8), 1.0)   # not 8-bit float codes
+    with pytest.raises(sa.AttnError):
+        sa.fwd_fp8v(q, q, v, 1.0, v_format="e3m4")

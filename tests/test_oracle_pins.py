@@ -537,8 +537,8 @@ def test_fp8_round_in_range_matches_library_and_saturates():
 
 
 def test_attn_dense_fp8v_definition():
-    """O1 with V as E4M3 codes times a scale: (a) equals O1 on the same values stored as bf16
-    (every E4M3 value with |v| <= 448 is a bf16 value), through a different decoder; (b) is linear
+    """O1 with V as 8-bit codes times a scale: (a) equals O1 on the same values stored as bf16
+    (every E4M3 and E5M2 value is a bf16 value), through a different decoder; (b) is linear
     in the scale (out halves, LSE unchanged); (c) equals a numpy float64 softmax-weighted sum with
     V decoded by torch's float8 type."""
     rng = np.random.default_rng(14)
@@ -555,6 +555,11 @@ def test_attn_dense_fp8v_definition():
         oh, lh = oracle.attn_dense_fp8v(q, k, codes, 0.5, causal=causal)
         np.testing.assert_allclose(oh, 0.5 * o8, rtol=0, atol=1e-15)
         np.testing.assert_array_equal(lh, l8)
+    c5 = oracle.round_fp8_bits(rng.standard_normal((B, N, H, D)).astype(np.float32), "e5m2")
+    v5 = torch.from_numpy(oracle.decode_bits(c5, "e5m2").astype(np.float32)).to(torch.bfloat16)
+    o5, l5 = oracle.attn_dense_fp8v(q, k, c5, 1.0, causal=True, v_format="e5m2")
+    ob5, lb5 = oracle.attn_dense(q, k, v5, causal=True)
+    np.testing.assert_allclose(o5, ob5, rtol=0, atol=1e-14)
     vt = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
     qd, kd = q.double().numpy(), k.double().numpy()
     s = np.einsum("bihd,bjhd->bhij", qd, kd) / np.sqrt(D)
