@@ -364,6 +364,30 @@ def test_masked_long_context_full_size(sa):
     _compare(out.reshape(-1, s["D"])[rt], lse.reshape(-1)[rt], ref, ref_lse, "bf16", "masked")
 
 
+def test_long_sequence_mask_past_32_bit_offsets(sa):
+    """N = 65536: a 4 GiB mask (row offsets beyond 2^32, so read from global memory with 64-bit
+    offsets) ANDed with causal; sampled rows, the first and the last among them, against the
+    oracle.  The mask is a fixed pattern (visible unless (i + 3 j) % 7 == 0, every 5000th row
+    fully masked) so that building it stays cheap."""
+    N, D = 65536, 64
+    rng = si.rng_for(90, 0)
+    q, k, v = (si.cast(x, "bf16") for x in si.draw_qkv(rng, (1, N, 1, D), (1, N, 1, D)))
+    j3 = (3 * np.arange(N, dtype=np.int64)) % 7
+    pattern = np.stack([((r + j3) % 7 != 0) for r in range(7)]).astype(np.uint8)   # row i uses i % 7
+    mask = np.empty((N, N), np.uint8)
+    for r0 in range(0, N, 4096):
+        mask[r0:r0 + 4096] = pattern[np.arange(r0, r0 + 4096) % 7]
+    mask[::5000] = 0
+    md = torch.from_numpy(mask).to(DEV)
+    out, lse = sa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, mask=md)
+    torch.cuda.synchronize()
+    del md
+    rows = np.unique(np.concatenate([si.rng_for(90, 1).integers(0, N, 48), [0, 1, 5000, 40000, N - 1]]))
+    ref, ref_lse = oracle.attn_dense(q, k, v, causal=True, mask=mask, rows=rows)
+    rt = torch.from_numpy(rows).to(DEV)
+    _compare(out.reshape(-1, D)[rt], lse.reshape(-1)[rt], ref, ref_lse, "bf16", "N=65536 masked")
+
+
 @pytest.mark.parametrize("D,BN", [(16, 32), (64, 64), (128, 64), (256, 64)])
 def test_mask_ragged_small(sa, D, BN):
     """Arbitrary masks with ragged N (odd lengths, unaligned mask rows) against the oracle."""
