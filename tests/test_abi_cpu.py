@@ -19,6 +19,44 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(sa.lib(), n), n
 
 
+@pytest.mark.parametrize("lang,std", [("c", "-std=c11"), ("c++", "-std=c++17")])
+def test_header_is_plain_c_and_cpp(lang, std, tmp_path):
+    """include/attn.h compiles on its own as C11 (no torch or C++ types in the boundary) and as
+    C++17, warning-free; a C program that calls every entry point links against libattn.so."""
+    import os
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("no host compiler")
+    hdr = os.path.join(os.path.dirname(sa.LIB_PATH), "..", "include", "attn.h")
+    r = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only", "-x", lang, hdr],
+                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout
+    if lang == "c":
+        src = tmp_path / "use.c"
+        src.write_text('#include "attn.h"\n'
+                       "int main(void) {\n"
+                       "  return attn_abi_version() == ATTN_ABI_VERSION &&\n"
+                       "         attn_fwd(0, 0, 0, 0, 0, 1, 1, 1, 64, 0, 0, ATTN_BF16, 0) == ATTN_E_NULL &&\n"
+                       "         attn_fwd_splitk(0, 0, 0, 0, 0, 1, 1, 1, 1, 64, 0, 0, 1, 0, 0, ATTN_BF16, 0) == ATTN_E_NULL &&\n"
+                       "         attn_fwd_splitk_fused(0, 0, 0, 0, 0, 1, 1, 1, 1, 64, 0, 0, 1, 0, 0, 0, ATTN_BF16, 0) == ATTN_E_NULL &&\n"
+                       "         attn_combine(0, 0, 0, 0, 1, 1, 1, 64, ATTN_FP32, 0) == ATTN_E_NULL &&\n"
+                       "         attn_softmax_rows(0, 0, 1, 1, ATTN_FP32, ATTN_SOFTMAX_STREAMING, 0) == ATTN_E_NULL &&\n"
+                       "         attn_fwd_fp8v(0, 0, 0, ATTN_FP8_E4M3, 1.0f, 0, 0, 1, 1, 1, 128, 0, 0, ATTN_BF16, 0) == ATTN_E_NULL &&\n"
+                       "         attn_round(0, 0, 4, ATTN_BF16, 0) == ATTN_E_NULL &&\n"
+                       "         attn_fwd_ex(0, 0) == ATTN_E_NULL && attn_last_error()[0] != 0 ? 0 : 1;\n"
+                       "}\n")
+        exe = tmp_path / "use"
+        libdir = os.path.dirname(sa.LIB_PATH)
+        r = subprocess.run([cc, std, "-Wall", "-Werror", "-I", os.path.dirname(hdr), str(src), "-o", str(exe),
+                            "-L", libdir, "-lattn", "-Wl,-rpath," + libdir],
+                           stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        assert r.returncode == 0, r.stdout
+        r = subprocess.run([str(exe)], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=60)
+        assert r.returncode == 0, r.stdout
+
+
 def test_abi_version():
     assert sa.attn_abi_version() == 1
 
