@@ -112,6 +112,19 @@ def fp8v_figures(sa, dev, steps=10, warmup=3, bf16_ms=None):
             "speedup_vs_bf16": None if bf16_ms is None else bf16_ms / m[0]}
 
 
+def combine_large_figures(sa, dev, sd, steps=10, warmup=3):
+    """attn_combine with P = 16 on rows 8192, the decode's heads and depth: a 2.2 GB workspace,
+    larger than the caches."""
+    Pc, rows_c = 16, 8192
+    opc = torch.randn((Pc, rows_c, sd["H"], sd["D"]), dtype=torch.float32, device=dev)
+    lpc = torch.randn((Pc, rows_c, sd["H"]), dtype=torch.float32, device=dev)
+    obc = torch.empty((rows_c, sd["H"], sd["D"]), dtype=torch.bfloat16, device=dev)
+    _, m = timed_events([lambda: sa.attn_combine(opc, lpc, obc)], steps, warmup)
+    cb = combine_bytes(Pc, rows_c * sd["H"], sd["D"])
+    return {"P": Pc, "rows": rows_c, "heads": sd["H"], "depth": sd["D"], "ms": m[0], "bytes": cb,
+            "GB/s": cb / (m[0] * 1e-3) / 1e9, "hbm_frac": cb / (m[0] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 def combine_cold_figures(sa, dev, sd):
     """attn_combine at the decode shape (rows B*Nq, heads H, depth D) for each P of the sweep,
     each call on a different workspace of a set larger than 1 GiB."""
@@ -258,7 +271,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "combine", "copy", "softmax", "fp8v", "masked"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "combine", "copy", "softmax", "fp8v", "masked", "combine_large"],
+                    default=None,
                     help="time a single kernel (for profiler runs); 'copy' times a plain 1 GiB device "
                          "copy, the calibration for the HBM byte counters")
     args = ap.parse_args()
@@ -281,6 +295,9 @@ def main():
         return
     if args.only == "softmax":
         print(json.dumps({"softmax": softmax_figures(sa, dev, args.steps, args.warmup)}), flush=True)
+        return
+    if args.only == "combine_large":
+        print(json.dumps({"combine_large": combine_large_figures(sa, dev, si.DECODE, args.steps, args.warmup)}), flush=True)
         return
     if args.only == "masked":
         print(json.dumps({"masked_long_context": masked_figures(sa, dev, args.steps, args.warmup)}), flush=True)
@@ -361,16 +378,7 @@ def main():
         #      separate workspaces (> 1 GiB) that each call reads from HBM, not the caches
         extra["combine_cold"] = combine_cold_figures(sa, dev, sd)
         # ---- combine on a workspace larger than the caches (rows 8192, heads 32, depth 128) -
-        Pc, rows_c = 16, 8192
-        opc = torch.randn((Pc, rows_c, sd["H"], sd["D"]), dtype=torch.float32, device=dev)
-        lpc = torch.randn((Pc, rows_c, sd["H"]), dtype=torch.float32, device=dev)
-        obc = torch.empty((rows_c, sd["H"], sd["D"]), dtype=torch.bfloat16, device=dev)
-        _, m = timed_events([lambda: sa.attn_combine(opc, lpc, obc)], 10, 3)
-        cb = combine_bytes(Pc, rows_c * sd["H"], sd["D"])
-        extra["combine_large"] = {"P": Pc, "rows": rows_c, "heads": sd["H"], "depth": sd["D"], "ms": m[0],
-                                  "GB/s": cb / (m[0] * 1e-3) / 1e9,
-                                  "hbm_frac": cb / (m[0] * 1e-3) / 1e9 / PEAK_HBM_GBS}
-        del opc, lpc, obc
+        extra["combine_large"] = combine_large_figures(sa, dev, sd)
         # ---- single-head shape, 32- vs 64-key tiles (context) --------------------------------
         extra["block_n_single_head_N2048_D64"] = block_n_figures(sa, dev)
         # ---- standalone row softmax (32768 rows x 4096 fp32; and 4096 x 32768) -------------
