@@ -366,7 +366,7 @@ def main():
             sweep[str(P)] = {"decode_ms": m[0], "decode_GB/s": decode_bytes(sd["B"], sd["H"], sd["Nkv"], sd["D"], P) / (m[0] * 1e-3) / 1e9,
                              "combine_ms": m[1], "combine_GB/s": combine_bytes(P, RH, sd["D"]) / (m[1] * 1e-3) / 1e9}
             # the same producer and merge in one launch (attn_fwd_splitk_fused)
-            tk = torch.zeros(RH, dtype=torch.int32, device=dev)
+            tk = torch.zeros(RH * sa.TICKET_STRIDE, dtype=torch.int32, device=dev)
             fl_ = torch.empty((sd["B"], sd["H"]), dtype=torch.float32, device=dev)
             _, mf = timed_events([lambda: sa.attn_fwd_splitk_fused(dq, dk, dv, P, op, lp, tk, ob, fl_)], 10, 3)
             fb = decode_bytes(sd["B"], sd["H"], sd["Nkv"], sd["D"], P) + combine_bytes(P, RH, sd["D"])

@@ -60,6 +60,7 @@ extern "C" {
 
 #define ATTN_ABI_VERSION 1
 #define ATTN_P_MAX 256 /* largest split count: one partition per MI355X compute unit */
+#define ATTN_TICKET_STRIDE 32 /* uint32 slots per row-head in a fused-decode ticket array (128 B) */
 
 enum attn_dtype {
   ATTN_BF16 = 0,
@@ -117,16 +118,19 @@ int attn_fwd_splitk(const void* q, const void* k, const void* v, void* out, floa
  * attn_fwd_splitk_fused -- attn_fwd_splitk followed by the combine, in ONE launch (the CDNA4
  *   counterpart of Modular MAX "fa4_splitk_combine"'s overlap of the combine with the producer's
  *   tail).  Each (row-head, partition) workgroup writes its workspace entry as attn_fwd_splitk
- *   does, makes it visible device-wide and increments tickets[rh]; the workgroup that takes the
- *   last ticket merges the P entries with attn_combine's formulas, writes out / lse and resets
- *   tickets[rh] to 0.  Every row-head runs on the bandwidth-bound decode kernel, so this is
+ *   does, makes it visible device-wide and increments its row-head's ticket; the workgroup that
+ *   takes the last ticket merges the P entries with attn_combine's formulas, writes out / lse and
+ *   resets the ticket to 0.  Every row-head runs on the bandwidth-bound decode kernel, so this is
  *   meant for few-query (decode) shapes.
  *   Arguments as attn_fwd_splitk, except:
  *   out          REQUIRED, [B, Nq, H, D] of `dtype`.
  *   lse          nullable; [B, Nq, H] float32, natural log.
- *   tickets      REQUIRED, uint32 [B * Nq * H], 4-byte aligned, caller-owned.  It must hold 0 in
- *                every entry before the first call (e.g. one hipMemset at allocation); a call that
- *                runs to completion leaves it at 0 again, so it is reusable without clearing.
+ *   tickets      REQUIRED, uint32 [B * Nq * H * ATTN_TICKET_STRIDE], 4-byte aligned,
+ *                caller-owned.  Row-head rh counts in tickets[rh * ATTN_TICKET_STRIDE]; the other
+ *                slots are padding that keeps every counter on its own 128-byte line (counters
+ *                that share a line serialise their atomics in the memory system).  It must hold 0
+ *                in every counter before the first call (e.g. one hipMemset at allocation); a call
+ *                that runs to completion leaves it at 0 again, so it is reusable without clearing.
  *                Two calls that overlap in time (different streams) must not share it.
  *   Errors: ATTN_E_WORKSPACE if o_partial, lse_partial or tickets is NULL; otherwise as
  *   attn_fwd_splitk and attn_combine.

@@ -17,7 +17,7 @@ Entry points (same names as the C ABI in include/attn.h):
     attn_last_error(), attn_abi_version()
 Tensors are torch tensors on the GPU, contiguous, laid out as the header states
 (q/out [B, Nq, H, D]; k/v [B, Nkv, H, D]; o_partial [P, B*Nq, H, D]; lse_partial [P, B*Nq, H];
-tickets int32 [B*Nq*H], zero before the first call and left zero by every call).
+tickets int32 [B*Nq*H*TICKET_STRIDE], zero before the first call and left zero by every call).
 Allocating helpers fwd(), fwd_fp8v(), splitk(), splitk_fused() and combine() return fresh outputs.
 """
 import ctypes
@@ -34,6 +34,7 @@ ATTN_BF16, ATTN_FP16, ATTN_FP32, ATTN_FP8_E4M3, ATTN_FP8_E5M2 = 0, 1, 2, 3, 4
 STATUS = {0: "ATTN_OK", 1: "ATTN_E_NULL", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUPPORTED",
           4: "ATTN_E_ALIGN", 5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
 P_MAX = 256
+TICKET_STRIDE = 32          # int32 slots per row-head in a fused-decode ticket array
 SOFTMAX_STREAMING, SOFTMAX_REGISTERS, SOFTMAX_THREE_PASS = 0, 1, 2
 
 
@@ -241,9 +242,10 @@ def softmax_rows(x, method=SOFTMAX_STREAMING):
 
 
 def tickets(q):
-    """A zeroed ticket array for attn_fwd_splitk_fused (reusable: every call leaves it zero)."""
+    """A zeroed ticket array for attn_fwd_splitk_fused (reusable: every call leaves it zero).
+    One counter per row-head, TICKET_STRIDE slots apart (one 128-byte line each)."""
     B, Nq, H, _ = q.shape
-    return torch.zeros(B * Nq * H, dtype=torch.int32, device=q.device)
+    return torch.zeros(B * Nq * H * TICKET_STRIDE, dtype=torch.int32, device=q.device)
 
 
 def splitk_fused(q, k, v, P, causal=False, mask=None, tk=None):

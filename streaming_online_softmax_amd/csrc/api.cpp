@@ -14,6 +14,9 @@
 #include "../../include/attn.h"
 #include "launch.h"
 
+static_assert(ATTN_P_MAX == attn::ATTN_P_MAX_DEV, "split bound differs between header and kernels");
+static_assert(ATTN_TICKET_STRIDE == attn::ATTN_TICKET_STRIDE_DEV, "ticket stride differs between header and kernels");
+
 namespace {
 
 thread_local char g_err[512] = "";

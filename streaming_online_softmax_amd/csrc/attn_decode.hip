@@ -159,76 +159,75 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecodeParams p) {
   for (int w = 0; w < 4; ++w) { aw[w] = fast_exp2(sm_m[w] - M_use); L += aw[w] * sm_l[w]; }
   const float inv = L == 0.f ? 0.f : 1.f / L;
   const int64_t prh = (int64_t)part * p.B * p.Nq * p.H + rh;
-  for (int d = tid; d < D; d += 256) {
-    float acc = 0.f;
+  if constexpr (!FUSED) {
+    for (int d = tid; d < D; d += 256) {
+      float acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) acc = fmaf(aw[w], sm_o[w][d], acc);
-    put_ws<FUSED>(p.o_partial + prh * D + d, acc * inv);
-  }
-  if (tid == 0) put_ws<FUSED>(p.lse_partial + prh, L == 0.f ? kNegInf : M_use + log2f(L));
-
-  if constexpr (FUSED) {
-    // ---- publish this partition, then count it.  The workspace entries above were written with
-    //      device-coherent stores (they bypass the per-XCD L2s, which are not coherent with one
-    //      another); each thread waits until its stores have completed, the barrier gathers the
-    //      workgroup, and one thread takes the ticket with a device-coherent atomic.  A workgroup
-    //      that draws the last ticket was therefore preceded by every other partition's completed
-    //      stores, and reads them back with device-coherent loads.  No cache-wide write-back or
-    //      invalidate is needed (an agent-scope release/acquire fence would do both, in every
-    //      workgroup, and costs more than the whole combine).
-    __shared__ int sm_last;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t t = __hip_atomic_fetch_add(p.tickets + rh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      sm_last = (t == (uint32_t)p.P - 1u);
+      for (int w = 0; w < 4; ++w) acc = fmaf(aw[w], sm_o[w][d], acc);
+      p.o_partial[prh * D + d] = acc * inv;
     }
-    __syncthreads();
-    if (!sm_last) return;
-    // ---- last partition of this row-head: merge the P entries
+    if (tid == 0) p.lse_partial[prh] = L == 0.f ? kNegInf : M_use + log2f(L);
+  } else {
+    // ---- publish this partition, then count it.  Only the first wave does this (the other
+    //      three leave now and free their slots for other workgroups): it writes the entry with
+    //      device-coherent stores (they bypass the per-XCD L2s, which are not coherent with one
+    //      another), waits until those stores have completed, and takes the row-head's ticket
+    //      with a device-coherent atomic.  The wave that draws the last ticket was therefore
+    //      preceded by every other partition's completed stores, and reads them back with
+    //      device-coherent loads.  No cache-wide write-back or invalidate is needed (an
+    //      agent-scope release/acquire fence would do both, in every workgroup).
+    if (wave != 0) return;
+    for (int d = lane; d < D; d += 64) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc = fmaf(aw[w], sm_o[w][d], acc);
+      put_ws<true>(p.o_partial + prh * D + d, acc * inv);
+    }
+    if (lane == 0) put_ws<true>(p.lse_partial + prh, L == 0.f ? kNegInf : M_use + log2f(L));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // keeps the stores before the ticket
+    __builtin_amdgcn_s_waitcnt(0);
+    uint32_t t = 0;
+    if (lane == 0) t = __hip_atomic_fetch_add(p.tickets + rh * ATTN_TICKET_STRIDE_DEV, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    t = __builtin_amdgcn_readfirstlane(t);
+    if (t != (uint32_t)p.P - 1u) return;
+    // ---- last partition of this row-head: merge the P entries in this wave
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     __shared__ float sc_tab[ATTN_P_MAX_DEV];
-    __shared__ float red[2][4];
-    __shared__ __attribute__((aligned(16))) float part_acc[1024];
     const int64_t RH = (int64_t)p.B * p.Nq * p.H;
-    // LSE phase: thread t holds partition t (P <= 256 = threads)
-    const float lsv = tid < p.P ? get_ws(p.lse_partial + (int64_t)tid * RH + rh) : kNegInf;
-    float wm = across_groups_max<1>(lsv);
-    if (lane == 0) red[0][wave] = wm;
-    __syncthreads();
-    const float mx = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    float e = (lsv == kNegInf) ? 0.f : fast_exp2(lsv - mx);
+    // LSE phase: lane holds partitions lane + 64 j (P <= 256)
+    float lsv[ATTN_P_MAX_DEV / 64];
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < ATTN_P_MAX_DEV / 64; ++j) {
+      const int pp = lane + 64 * j;
+      lsv[j] = pp < p.P ? get_ws(p.lse_partial + (int64_t)pp * RH + rh) : kNegInf;
+      mx = fmaxf(mx, lsv[j]);
+    }
+    mx = across_groups_max<1>(mx);
+    float e = 0.f;
+#pragma unroll
+    for (int j = 0; j < ATTN_P_MAX_DEV / 64; ++j) e += (lsv[j] == kNegInf) ? 0.f : fast_exp2(lsv[j] - mx);
     e = group_sum<64>(e);
-    if (lane == 0) red[1][wave] = e;
-    __syncthreads();
-    const float sum = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
     const bool empty = (mx == kNegInf);
-    const float Gl = empty ? kNegInf : log2f(sum) + mx;
-    if (tid < p.P) sc_tab[tid] = (empty || lsv == kNegInf) ? 0.f : fast_exp2(lsv - Gl);
-    __syncthreads();
-    // weighted sum: thread -> (4-element slice c, partition group pg); groups then folded in LDS
-    constexpr int NC = D / 4, NG = 256 / NC;
-    const int c4 = tid % NC, pg = tid / NC;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    const float* src = p.o_partial + rh * D + 4 * c4;
-    for (int pp = pg; pp < p.P; pp += NG) {
-      const float sp = sc_tab[pp];
-      if (sp != 0.f) {   // an empty partition adds nothing
-        const float* e4 = src + (int64_t)pp * RH * D;
-        acc += sp * f32x4{get_ws(e4), get_ws(e4 + 1), get_ws(e4 + 2), get_ws(e4 + 3)};
+    const float Gl = empty ? kNegInf : log2f(e) + mx;
+#pragma unroll
+    for (int j = 0; j < ATTN_P_MAX_DEV / 64; ++j) {
+      const int pp = lane + 64 * j;
+      if (pp < p.P) sc_tab[pp] = (empty || lsv[j] == kNegInf) ? 0.f : fast_exp2(lsv[j] - Gl);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");   // the table is complete before it is read
+    // weighted sum: lane covers d = lane + 64 i
+    for (int d = lane; d < D; d += 64) {
+      float acc = 0.f;
+      for (int pp = 0; pp < p.P; ++pp) {
+        const float sp = sc_tab[pp];
+        if (sp != 0.f) acc = fmaf(sp, get_ws(p.o_partial + ((int64_t)pp * RH + rh) * D + d), acc);   // empty adds nothing
       }
+      ((uint16_t*)p.out)[rh * D + d] = (uint16_t)(E::pack2(acc, 0.f) & 0xFFFFu);
     }
-    *reinterpret_cast<f32x4*>(part_acc + 4 * tid) = acc;
-    __syncthreads();
-    if (tid < NC) {
-      f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int g2 = 0; g2 < NG; ++g2) r += *reinterpret_cast<const f32x4*>(part_acc + 4 * (g2 * NC + tid));
-      *reinterpret_cast<u32x2*>((uint16_t*)p.out + rh * D + 4 * tid) = u32x2{E::pack2(r[0], r[1]), E::pack2(r[2], r[3])};
-    }
-    if (tid == 0) {
+    if (lane == 0) {
       if (p.lse) p.lse[rh] = empty ? kNegInf : Gl * kLn2;
-      __hip_atomic_store(p.tickets + rh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
+      __hip_atomic_store(p.tickets + rh * ATTN_TICKET_STRIDE_DEV, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
     }
   }
 }

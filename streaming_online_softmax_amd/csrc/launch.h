@@ -6,6 +6,7 @@
 namespace attn {
 
 constexpr int ATTN_P_MAX_DEV = 256;   // largest split count (one partition per compute unit)
+constexpr int ATTN_TICKET_STRIDE_DEV = 32;   // uint32 slots per row-head ticket: one 128-byte line each
 
 // Tiled matrix-core forward (attn_fwd, and the split-K producer when Nq > 1).
 struct FwdParams {
@@ -43,10 +44,11 @@ struct DecodeParams {
   int chunk;
   float scale_log2;
   // fused combine (attn_fwd_splitk_fused): the last workgroup of each row-head merges the
-  // workspace into out / lse; tickets[rh] counts finished partitions and is returned to 0
+  // workspace into out / lse; tickets[rh * ATTN_TICKET_STRIDE_DEV] counts finished partitions
+  // and is returned to 0
   void* out;            // [B, Nq, H, D] input dtype
   float* lse;           // [B, Nq, H] natural log, nullable
-  uint32_t* tickets;    // [B * Nq * H], zero on entry and on exit
+  uint32_t* tickets;    // [B * Nq * H * ATTN_TICKET_STRIDE_DEV], counters zero on entry and exit
 };
 
 // LSE-weighted combine of a split-K workspace.

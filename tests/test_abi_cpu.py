@@ -61,6 +61,22 @@ def test_abi_version():
     assert sa.attn_abi_version() == 1
 
 
+def test_binding_constants_match_the_header():
+    """The binding's copies of the header's sizes and codes are the header's values."""
+    import re
+    with open(sa.HEADER) as f:
+        text = f.read()
+    defines = dict((n, int(v)) for n, v in re.findall(r"^#define (ATTN_\w+) (\d+)", text, re.M))
+    enums = dict((n, int(v)) for n, v in re.findall(r"\b(ATTN_[A-Z0-9_]+) = (\d+)", text))
+    assert defines["ATTN_P_MAX"] == sa.P_MAX
+    assert defines["ATTN_TICKET_STRIDE"] == sa.TICKET_STRIDE
+    assert defines["ATTN_ABI_VERSION"] == sa.attn_abi_version()
+    for name in ("ATTN_BF16", "ATTN_FP16", "ATTN_FP32", "ATTN_FP8_E4M3", "ATTN_FP8_E5M2",
+                 "ATTN_SOFTMAX_STREAMING", "ATTN_SOFTMAX_REGISTERS", "ATTN_SOFTMAX_THREE_PASS"):
+        binding = name[len("ATTN_"):] if name.startswith("ATTN_SOFTMAX") else name
+        assert enums[name] == getattr(sa, binding), name
+
+
 needs_no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
                                   reason="fake-pointer reject paths run only where no GPU is visible")
 

@@ -29,7 +29,7 @@ def test_captured_forward_split_combine_fused_replays(sa):
     l_p = torch.empty((P, 2, 4), dtype=torch.float32, device=DEV)
     dout = torch.empty((2, 1, 4, 128), dtype=torch.bfloat16, device=DEV)
     dlse = torch.empty((2, 1, 4), dtype=torch.float32, device=DEV)
-    tk = torch.zeros(8, dtype=torch.int32, device=DEV)
+    tk = torch.zeros(8 * sa.TICKET_STRIDE, dtype=torch.int32, device=DEV)
     fout = torch.empty_like(dout)
     flse = torch.empty_like(dlse)
     fo_p, fl_p = torch.empty_like(o_p), torch.empty_like(l_p)

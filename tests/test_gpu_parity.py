@@ -263,7 +263,7 @@ def test_decode_fused_reuses_tickets(sa):
     """Two fused calls in a row on one ticket array, the second smaller (fewer partitions, other
     data, fp16): both match the oracle and the tickets are 0 after each."""
     rng = si.rng_for(88, 0)
-    tk = torch.zeros(2 * 1 * 8, dtype=torch.int32, device=DEV)
+    tk = torch.zeros(2 * 1 * 8 * sa.TICKET_STRIDE, dtype=torch.int32, device=DEV)
     for P, n, dt in ((13, 3000, "bf16"), (5, 700, "f16")):
         q, k, v = (si.cast(x, dt) for x in si.draw_qkv(rng, (2, 1, 8, 64), (2, n, 8, 64)))
         out, lse, _, _ = sa.splitk_fused(q.to(DEV), k.to(DEV), v.to(DEV), P, tk=tk)
