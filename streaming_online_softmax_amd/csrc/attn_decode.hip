@@ -12,8 +12,9 @@
 // key chunks and are merged once at the end with the same rescale rule (Tylo.jl "Streaming
 // attention and online state", section "Online statistics", merge of two summaries).
 //
-// Fused form (FUSED): after writing its workspace entry, each workgroup takes a ticket for its
-// row-head; the one that takes the last ticket merges all P entries with the LSE-weighted
+// Fused form (FUSED): after writing its workspace entry, each workgroup takes a ticket from its
+// row-head's counter (one counter per 128-byte line: counters sharing a line serialise their
+// atomics); the one that takes the last ticket merges all P entries with the LSE-weighted
 // combine (Modular MAX "fa4_splitk_combine", per-row-head formulas) and writes the output, so
 // decode is one launch instead of producer + combine.  This is the one-GPU stand-in for the
 // page's programmatic launch overlap of the combine with the producer's tail.
