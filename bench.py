@@ -15,8 +15,10 @@ fp32 rows, the masked long-context prefill (B1 H16 N16384 D256, causal AND a Ber
 mask with 1/64 of the rows fully masked) beside the same shape without the mask, the prefill
 with E4M3 V on the FP8 matrix cores (attn_fwd_fp8v), the decode-shape combine on cold workspaces
 (cycling through more than 1 GiB of them), 32- vs 64-key tiles on a single-head N2048 D64 shape,
-and the shader clock rocm-smi reports right after the timed region.  Every per-kernel time comes from HIP events recorded on the
-stream the kernels are launched on, over the whole timed region.  Rank 0 prints one JSON line.
+and the shader clock rocm-smi reports right after the timed region.  Every per-kernel time comes
+from HIP events recorded on the stream the kernels are launched on, around each launch of the
+timed region (default 50 steps after 5 warm-up steps): mean, median and minimum per kernel.
+Rank 0 prints one JSON line.
 """
 import argparse
 import hashlib
@@ -218,9 +220,10 @@ def measured_traffic():
         return None
 
 
-def timed_events(fn_list, steps, warmup):
+def timed_events(fn_list, steps, warmup, stats=None):
     """Run the list of callables once per step; returns (wall seconds for `steps` steps,
-    per-callable mean milliseconds from events on the current stream)."""
+    per-callable mean milliseconds from events on the current stream).  With a dict `stats`,
+    also stores the per-callable median and minimum (ms) there under "median" and "min"."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         for fn in fn_list:
@@ -236,7 +239,11 @@ def timed_events(fn_list, steps, warmup):
             ev[s][j][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = [float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(steps)])) for j in range(len(fn_list))]
+    per = [[ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(steps)] for j in range(len(fn_list))]
+    ms = [float(np.mean(x)) for x in per]
+    if stats is not None:
+        stats["median"] = [float(np.median(x)) for x in per]
+        stats["min"] = [float(np.min(x)) for x in per]
     return wall, ms
 
 
@@ -268,7 +275,7 @@ def cpu_baseline(q, k, v, budget_s=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "combine", "copy", "softmax", "fp8v", "masked", "combine_large"],
@@ -334,7 +341,8 @@ def main():
     fns = {"prefill": [k_prefill], "decode": [k_decode], "combine": [k_decode, k_combine]}.get(
         args.only, [k_prefill, k_decode, k_combine])
     torch.cuda.synchronize()
-    wall, ms = timed_events(fns, args.steps, args.warmup)
+    kstats = {}
+    wall, ms = timed_events(fns, args.steps, args.warmup, stats=kstats)
     clock = gpu_clock()
     assert not torch.isnan(out).any() and not torch.isnan(dout).any(), "NaN in outputs"
 
@@ -404,6 +412,8 @@ def main():
                    "step": "attn_fwd(prefill) + attn_fwd_splitk(decode B8 H32 Nq1 Nkv32768 D128 bf16, P=16) + attn_combine",
                    "B": sp["B"], "H": sp["H"], "N": sp["N"], "D": sp["D"], "causal": True},
         "kernel_ms": t,
+        "kernel_ms_median": dict(zip(names, kstats["median"])),
+        "kernel_ms_min": dict(zip(names, kstats["min"])),
         "gpu_clock_after_timing": clock,
         "roofline": None,
         "decode": None if "decode" not in t else {
