@@ -284,8 +284,8 @@ def main():
                          "copy, the calibration for the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(multi-GPU sharding is described, not built)", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path: each GPU would run its own share)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
