@@ -273,6 +273,26 @@ def test_decode_fused_reuses_tickets(sa):
         _compare(out.reshape(16, -1), lse.reshape(-1), ref, ref_lse, dt, f"fused P={P} n={n}")
 
 
+@pytest.mark.parametrize("D,P,Nkv", [(32, 255, 2049), (256, 256, 4100), (256, 7, 1000), (128, 64, 64 * 40 + 3)])
+def test_decode_fused_depths_and_split_bounds(sa, D, P, Nkv):
+    """Fused decode at the largest split count (every lane of the merging wave holds four
+    partitions' LSEs), ragged counts, depths below one wave (lanes past D idle in the merge) and
+    at 256 (four depth slices per lane); the workspace equals the two-launch producer's, the
+    output matches the oracle, the tickets end at 0."""
+    rng = si.rng_for(90, D * 1000 + P)
+    B, H = 2, 4
+    q, k, v = (si.cast(x, "f16") for x in si.draw_qkv(rng, (B, 1, H, D), (B, Nkv, H, D)))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    tk = sa.tickets(qd)
+    out, lse, o_p, l_p = sa.splitk_fused(qd, kd, vd, P, tk=tk)
+    o_u, l_u, _, _ = sa.splitk(qd, kd, vd, P)
+    torch.cuda.synchronize()
+    assert int(tk.abs().sum()) == 0
+    assert torch.equal(o_p, o_u) and torch.equal(l_p, l_u)
+    ref, ref_lse = oracle.attn_dense(q, k, v)
+    _compare(out.reshape(B * H, -1), lse.reshape(-1), ref, ref_lse, "f16", f"fused D={D} P={P} Nkv={Nkv}")
+
+
 def test_decode_fused_empty_and_masked(sa):
     """Fused decode with more partitions than keys, and with a byte mask that hides every key of
     one row-head's query (output 0, lse -inf), and with a few queries per head (Nq = 3)."""
@@ -296,7 +316,7 @@ def test_decode_fused_empty_and_masked(sa):
 @pytest.mark.parametrize("P,D", [(1, 64), (200, 128), (256, 16)])
 def test_decode_fused_partition_extremes(sa, P, D):
     """Fused decode at one partition (the merge is the identity) and at up to 256 partitions
-    (one per thread of the merging workgroup), with causal square shapes (Nq = Nkv = 3) too."""
+    (four per lane of the merging wave), with causal square shapes (Nq = Nkv = 3) too."""
     rng = si.rng_for(92, P)
     q, k, v = (si.cast(x, "bf16") for x in si.draw_qkv(rng, (2, 1, 4, D), (2, 3000, 4, D)))
     out, lse, _, _ = sa.splitk_fused(q.to(DEV), k.to(DEV), v.to(DEV), P)
