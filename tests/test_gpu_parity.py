@@ -3,10 +3,15 @@
 Tolerances: max |O_gpu - O_oracle| <= 2e-2 (bf16) / 5e-3 (fp16) over all compared elements;
 |LSE_gpu - LSE_oracle| <= 1e-3 * max(1, |LSE|); an all-masked row must give O exactly 0 and
 LSE exactly -inf; split-K combined must match the unsplit result to 1e-3.  The oracle is fed the
-exact bf16/fp16 values the kernels read.  Full-size workloads compare sampled rows (seeded),
-which the oracle computes one by one, plus properties that hold at any size.
+exact bf16/fp16 values the kernels read.  The full-size workloads (causal prefill, split-K decode
+at every split count, masked long context) compare every row-head with the oracle, in chunks of
+rows; each such test prints its largest error over all rows (and, when ATTN_PARITY_REPORT names a
+file, appends it there as one JSON line).
 """
+import json
 import math
+import os
+import time
 
 import numpy as np
 import pytest
@@ -44,6 +49,51 @@ def _compare(out, lse, ref, ref_lse, dtype, what=""):
         lerr = np.abs(l[fin] - ref_lse[fin]) / np.maximum(1.0, np.abs(ref_lse[fin]))
         assert (lerr.max() if lerr.size else 0.0) <= 1e-3, f"{what}: LSE rel err {lerr.max():.3e}"
     return err
+
+
+def _report(name, **fields):
+    line = {"test": name, **fields}
+    print("parity:", json.dumps(line), flush=True)
+    path = os.environ.get("ATTN_PARITY_REPORT")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(line) + "\n")
+
+
+def _full_compare(out, lse, q, k, v, dtype, name, causal=False, mask=None, chunk=1 << 16):
+    """Every row-head of out [B, N, H, D] / lse [B, N, H] (GPU tensors) against O1, the oracle
+    run over contiguous chunks of row-heads.  Returns the worst errors and where they occur."""
+    D = q.shape[-1]
+    o_all = out.reshape(-1, D).float().cpu().numpy()
+    l_all = lse.reshape(-1).cpu().numpy()
+    n = o_all.shape[0]
+    worst = {"rows": n, "max_abs_err": 0.0, "at_row": -1, "abs_O_there": 0.0, "max_lse_rel_err": 0.0,
+             "empty_rows": 0}
+    t0 = time.perf_counter()
+    for r0 in range(0, n, chunk):
+        rows = np.arange(r0, min(n, r0 + chunk), dtype=np.int64)
+        ref, ref_lse = oracle.attn_dense(q, k, v, causal=causal, mask=mask, rows=rows)
+        o = o_all[rows].astype(np.float64)
+        l = l_all[rows].astype(np.float64)
+        assert not np.isnan(o).any(), f"{name}: NaN in rows {r0}.."
+        e = np.abs(o - ref)
+        i = int(np.argmax(e.max(axis=1)))
+        if e[i].max() > worst["max_abs_err"]:
+            worst.update(max_abs_err=float(e[i].max()), at_row=int(rows[i]),
+                         abs_O_there=float(np.abs(ref[i]).max()))
+        empty = ref_lse == -np.inf
+        worst["empty_rows"] += int(empty.sum())
+        assert np.all(o[empty] == 0.0), f"{name}: all-masked rows not exactly 0"
+        assert np.all(l[empty] == -np.inf), f"{name}: all-masked rows LSE not -inf"
+        fin = ~empty
+        if fin.any():
+            lerr = np.abs(l[fin] - ref_lse[fin]) / np.maximum(1.0, np.abs(ref_lse[fin]))
+            worst["max_lse_rel_err"] = max(worst["max_lse_rel_err"], float(lerr.max()))
+    worst["oracle_s"] = round(time.perf_counter() - t0, 1)
+    _report(name, dtype=dtype, **worst)
+    assert worst["max_abs_err"] <= TOL[dtype], f"{name}: max|dO|={worst['max_abs_err']:.3e} at row {worst['at_row']}"
+    assert worst["max_lse_rel_err"] <= 1e-3, f"{name}: LSE rel err {worst['max_lse_rel_err']:.3e}"
+    return worst
 
 
 # ---------------------------------------------------------------------------------------------
@@ -136,6 +186,81 @@ def test_d128_split(sa, P, causal):
 
 
 # ---------------------------------------------------------------------------------------------
+# D = 256 without a mask: the unmasked two-stage tile body and the lazy-rescale weight-sum test
+# on fully visible tiles (a mask always forces the exact test), ragged lengths, both dtypes
+# ---------------------------------------------------------------------------------------------
+D256_CASES = [(N, dt, causal, var) for N in (333, 1000, 2048) for dt in ("bf16", "f16")
+              for causal in (False, True) for var in ("normal",)] + \
+             [(1000, dt, causal, "large") for dt in ("bf16", "f16") for causal in (False, True)]
+
+
+@pytest.mark.parametrize("N,dtype,causal,variant", D256_CASES,
+                         ids=[f"N{n}-{d}-{'causal' if c else 'full'}-{v}" for n, d, c, v in D256_CASES])
+def test_d256_unmasked(sa, N, dtype, causal, variant):
+    rng = si.rng_for(93, N)
+    q, k, v = (si.cast(x, dtype) for x in si.draw_qkv(rng, (1, N, 2, 256), (1, N, 2, 256), variant))
+    out, lse = sa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+    ref, ref_lse = oracle.attn_dense(q, k, v, causal=causal)
+    _compare(out.reshape(-1, 256), lse.reshape(-1), ref, ref_lse, dtype, f"D256 N={N} {dtype} causal={causal} {variant}")
+
+
+def test_d256_causal_long_context_sampled(sa):
+    """The masked long-context tensors (B1 H16 N16384 D256) without the mask: causal only, the
+    unmasked D = 256 kernel at full size.  Four rows of every (128-row query block, head) unit, one
+    in each wave's 32 rows at a seeded lane, so every workgroup and every wave is checked."""
+    s = si.MASKED
+    q, k, v, _, _ = si.masked_inputs()
+    N, H, D = s["N"], s["H"], s["D"]
+    out, lse = sa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True)
+    torch.cuda.synchronize()
+    rng = si.rng_for(94, 0)
+    blocks = np.arange(N // 128)
+    i = (blocks[:, None, None] * 128 + np.arange(4)[None, :, None] * 32
+         + rng.integers(0, 32, (blocks.size, 4, H))).reshape(-1)
+    h = np.broadcast_to(np.arange(H)[None, None, :], (blocks.size, 4, H)).reshape(-1)
+    rows = np.unique(i * H + h)
+    ref, ref_lse = oracle.attn_dense(q, k, v, causal=True, rows=rows)
+    rt = torch.from_numpy(rows).to(DEV)
+    err = _compare(out.reshape(-1, D)[rt], lse.reshape(-1)[rt], ref, ref_lse, "bf16", "D256 causal long context")
+    _report("d256_causal_long_context_sampled", dtype="bf16", rows=int(rows.size), max_abs_err=float(err))
+
+
+# ---------------------------------------------------------------------------------------------
+# split-K with several queries and a different key length (the matrix-core split producer on
+# rectangular shapes): per-partition key ranges, ragged partitions, mask rows of [Nq, Nkv]
+# staged through LDS (Nkv and the partition length multiples of 16), read 8 bytes at a time or
+# bytewise
+# ---------------------------------------------------------------------------------------------
+RECT_CASES = [(3, 2000, 64, 5, False), (3, 2000, 64, 5, True), (77, 1000, 128, 3, False),
+              (77, 2048, 128, 8, True), (300, 1000, 64, 8, True), (300, 2000, 128, 3, False),
+              (77, 1000, 256, 3, True), (130, 777, 32, 4, True)]
+
+
+@pytest.mark.parametrize("Nq,Nkv,D,P,masked", RECT_CASES,
+                         ids=[f"Nq{a}-Nkv{b}-D{c}-P{d}-{'mask' if m else 'nomask'}" for a, b, c, d, m in RECT_CASES])
+def test_splitk_rectangular(sa, Nq, Nkv, D, P, masked):
+    rng = si.rng_for(95, Nq * 7 + Nkv + D + P)
+    B, H = 2, 3
+    q, k, v = (si.cast(x, "bf16") for x in si.draw_qkv(rng, (B, Nq, H, D), (B, Nkv, H, D)))
+    mask = None
+    md = None
+    if masked:
+        mask, _ = si.bernoulli_mask(rng, Nq, Nkv, 1)
+        md = torch.from_numpy(mask).to(DEV)
+    o_p, l_p, out, lse = sa.splitk(q.to(DEV), k.to(DEV), v.to(DEV), P, mask=md)
+    torch.cuda.synchronize()
+    ref_op, ref_lp = oracle.splitk(q, k, v, P, mask=mask)
+    for pp in range(P):
+        _compare(o_p[pp].reshape(-1, D), None, ref_op[pp], ref_lp[pp], "bf16", f"o_partial p={pp}")
+        lp = l_p[pp].reshape(-1).cpu().numpy().astype(np.float64)
+        fin = np.isfinite(ref_lp[pp])
+        assert np.all(lp[~fin] == -np.inf)
+        np.testing.assert_allclose(lp[fin], ref_lp[pp][fin], rtol=1e-4, atol=1e-4)
+    ref, ref_lse = oracle.attn_dense(q, k, v, mask=mask)
+    _compare(out.reshape(-1, D), lse.reshape(-1), ref, ref_lse, "bf16", f"rectangular Nq={Nq} Nkv={Nkv} P={P}")
+
+
+# ---------------------------------------------------------------------------------------------
 # causal future-V perturbation (workshop checker)
 # ---------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("D", [64, 128])
@@ -158,30 +283,12 @@ def test_future_perturbation_bitwise(sa, D):
 # ---------------------------------------------------------------------------------------------
 # multi-head causal prefill B4 H32 N4096 D128 bf16 (the benchmark's launch configuration)
 # ---------------------------------------------------------------------------------------------
-def _sample_rows(rng, B, N, H, n, extra_rows=()):
-    b = rng.integers(0, B, n)
-    i = rng.integers(0, N, n)
-    h = rng.integers(0, H, n)
-    for r in extra_rows:
-        b = np.append(b, [0, B - 1])
-        i = np.append(i, [r, r])
-        h = np.append(h, [0, H - 1])
-    return np.unique((b * N + i) * H + h)
-
-
 def test_prefill_full_size(sa):
-    s = si.PREFILL
+    """Every one of the 524,288 row-heads of the benchmark's launch against the oracle."""
     q, k, v = si.prefill_inputs()
-    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
-    out, lse = sa.fwd(qd, kd, vd, causal=True)
+    out, lse = sa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True)
     torch.cuda.synchronize()
-    assert not torch.isnan(out).any() and bool(torch.isfinite(lse).all())
-    rows = _sample_rows(si.rng_for(83, 0), s["B"], s["N"], s["H"], 384,
-                        extra_rows=(0, 1, 127, 128, 2047, 4095))
-    ref, ref_lse = oracle.attn_dense(q, k, v, causal=True, rows=rows)
-    o = out.reshape(-1, s["D"])[torch.from_numpy(rows).to(DEV)]
-    l = lse.reshape(-1)[torch.from_numpy(rows).to(DEV)]
-    _compare(o, l, ref, ref_lse, "bf16", "prefill")
+    _full_compare(out, lse, q, k, v, "bf16", "prefill_B4H32N4096D128_causal_all_rows", causal=True)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -190,13 +297,17 @@ def test_prefill_full_size(sa):
 @pytest.fixture(scope="module")
 def decode_data(sa):
     q, k, v = si.decode_inputs()
-    return q, k, v, q.to(DEV), k.to(DEV), v.to(DEV)
+    ref, ref_lse = oracle.attn_dense(q, k, v)          # every one of the 256 row-heads
+    return q, k, v, q.to(DEV), k.to(DEV), v.to(DEV), ref, ref_lse
 
 
 @pytest.mark.parametrize("P", [4, 8, 16, 37])
 def test_decode_splitk_full_size(sa, decode_data, P):
+    """Every row-head and every partition: o_partial and lse_partial against the oracle's
+    per-partition definition, the merged output against O1, and the split result against the
+    unsplit one (a single partition) to 1e-3 in FP32."""
     s = si.DECODE
-    q, k, v, qd, kd, vd = decode_data
+    q, k, v, qd, kd, vd, ref, ref_lse = decode_data
     o_p, l_p, out, lse = sa.splitk(qd, kd, vd, P)
     # unsplit reference on the GPU: one partition (the combine is then the identity)
     o1, l1, _, _ = sa.splitk(qd, kd, vd, 1, combine=False)
@@ -205,15 +316,15 @@ def test_decode_splitk_full_size(sa, decode_data, P):
     RH = s["B"] * s["H"]
     d = (out_f32.reshape(RH, -1) - o1.reshape(RH, -1)).abs().max().item()
     assert d <= 1e-3, f"split vs unsplit {d:.3e}"
-    rows = np.unique(si.rng_for(84, P).integers(0, RH, 48))
-    ref_op, ref_lp = oracle.splitk(q, k, v, P, rows=rows)
-    rt = torch.from_numpy(rows).to(DEV)
+    ref_op, ref_lp = oracle.splitk(q, k, v, P)
+    worst_p = 0.0
     for p in range(P):
-        _compare(o_p[p].reshape(RH, -1)[rt], None, ref_op[p], ref_lp[p], "bf16", f"o_partial p={p}")
-        lp = l_p[p].reshape(-1)[rt].cpu().numpy().astype(np.float64)
+        worst_p = max(worst_p, _compare(o_p[p].reshape(RH, -1), None, ref_op[p], ref_lp[p], "bf16", f"o_partial p={p}"))
+        lp = l_p[p].reshape(-1).cpu().numpy().astype(np.float64)
         np.testing.assert_allclose(lp, ref_lp[p], rtol=1e-4, atol=1e-4)
-    ref, ref_lse = oracle.attn_dense(q, k, v, rows=rows)
-    _compare(out.reshape(RH, -1)[rt], lse.reshape(-1)[rt], ref, ref_lse, "bf16", f"combined P={P}")
+    err = _compare(out.reshape(RH, -1), lse.reshape(-1), ref, ref_lse, "bf16", f"combined P={P}")
+    _report(f"decode_B8H32Nkv32768D128_P{P}_all_rows", dtype="bf16", rows=RH, max_abs_err_o_partial=float(worst_p),
+            max_abs_err_combined=float(err), split_vs_unsplit_fp32=float(d))
 
 
 def test_decode_empty_partitions(sa):
@@ -237,9 +348,9 @@ def test_decode_fused_full_size(sa, decode_data, P):
     """attn_fwd_splitk_fused: one launch; the workspace equals the unfused producer's bit for
     bit (same code); the merged output matches the two-launch path to one bf16 unit in the last
     place (their FP32 merge orders differ, so the two FP32 values may round to neighbouring bf16
-    numbers) and the oracle on sampled rows; tickets end at 0."""
+    numbers) and the oracle on every row-head; tickets end at 0."""
     s = si.DECODE
-    q, k, v, qd, kd, vd = decode_data
+    q, k, v, qd, kd, vd, ref, ref_lse = decode_data
     tk = sa.tickets(qd)
     out, lse, o_p, l_p = sa.splitk_fused(qd, kd, vd, P, tk=tk)
     o_u, l_u, out_u, lse_u = sa.splitk(qd, kd, vd, P)
@@ -253,10 +364,7 @@ def test_decode_fused_full_size(sa, decode_data, P):
     assert bool((same_sign & (ulps <= 1)).all()), f"max {int(ulps.max())} bf16 ulps apart"
     assert int((ulps > 0).sum()) < a.numel() // 100
     assert torch.allclose(lse, lse_u, rtol=1e-6, atol=1e-6)
-    rows = np.unique(si.rng_for(87, P).integers(0, RH, 48))
-    ref, ref_lse = oracle.attn_dense(q, k, v, rows=rows)
-    rt = torch.from_numpy(rows).to(DEV)
-    _compare(out.reshape(RH, -1)[rt], lse.reshape(-1)[rt], ref, ref_lse, "bf16", f"fused P={P}")
+    _compare(out.reshape(RH, -1), lse.reshape(-1), ref, ref_lse, "bf16", f"fused P={P}")
 
 
 def test_decode_fused_reuses_tickets(sa):
@@ -330,27 +438,57 @@ def test_decode_fused_partition_extremes(sa, P, D):
     _compare(out.reshape(6, -1), lse.reshape(-1), ref, ref_lse, "f16", f"fused causal P={min(P, 5)}")
 
 
+def _weighted_abs_v(q, k, v, causal):
+    """E[rh, d] = sum_j (w_j / L) |v_jd| with the exact weights w_j = exp(s_j - M) of each row
+    (float64, numpy; the sensitivity of O to relative perturbations of the weights)."""
+    qd, kd, vd = (t.double().numpy() for t in (q, k, v))
+    B, N, H, D = qd.shape
+    E = np.zeros((B, N, H, D))
+    for b in range(B):
+        for h in range(H):
+            s = qd[b, :, h, :] @ kd[b, :, h, :].T / np.sqrt(D)
+            if causal:
+                s = np.where(np.tri(N, dtype=bool), s, -np.inf)
+            w = np.exp(s - s.max(axis=1, keepdims=True))
+            E[b, :, h, :] = (w / w.sum(axis=1, keepdims=True)) @ np.abs(vd[b, :, h, :])
+    return E.reshape(B * N * H, D)
+
+
 @pytest.mark.parametrize("P", [1, 3, 7])
 def test_square_causal_split_matches_unsplit(sa, P):
-    """Square causal shapes through the matrix-core split path.  Here |O| reaches ~3 and the
-    split and unsplit results each carry their own bf16 rounding of the weights (<= 2^-9 * max|v|
-    per result, tile boundaries differ), so they are compared with each other within twice that
-    bound plus the unsplit output's bf16 rounding, and each against the oracle.  The 1e-3
-    split-vs-unsplit criterion is checked on the decode workload, where |O| ~ 1e-2."""
+    """Square causal shapes through the matrix-core split path, split (P partitions merged in
+    FP32) against unsplit (one partition, FP32 workspace: no output rounding on either side).
+    Each side rounds every weight p_j to bf16 before the P.V product against its own reference
+    maximum (relative error <= u = 2^-8, 8 significand bits) while l sums the unrounded weights,
+    so O_x - O = sum_j (p_j / l) d_j v_j with |d_j| <= u, and per element
+        |O_split - O_unsplit| <= 2 u E[rh, d] + 2^-14 E[rh, d] + 1e-6,
+    E = sum_j (w_j / L) |v_jd| (exact weights; 2^-14 E covers FP32 accumulation and the merge's
+    exponentials).  Here |O| reaches ~3 (rows with few keys), so the benchmark spec's 1e-3 applies to
+    the decode workload (|O| ~ 1e-2), where it is checked directly.  Both sides and attn_fwd are
+    also compared with the oracle."""
     rng = si.rng_for(86, P)
     N, D = 1000, 64
     q, k, v = (si.cast(x, "bf16") for x in si.draw_qkv(rng, (2, N, 4, D), (2, N, 4, D)))
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     o_p, l_p, _, _ = sa.splitk(qd, kd, vd, P, causal=True, combine=False)
     out32, lse32 = sa.combine(o_p, l_p, torch.float32)
+    o1, l1, _, _ = sa.splitk(qd, kd, vd, 1, causal=True, combine=False)
     out, lse = sa.fwd(qd, kd, vd, causal=True)
     torch.cuda.synchronize()
-    out32, lse32 = out32.reshape(out.shape), lse32.reshape(lse.shape)   # [B*Nq, H, ...] -> [B, Nq, H, ...]
-    d = (out32 - out.float()).abs()
-    vmax = float(v.float().abs().max())
-    bound = 2 * 2.0 ** -9 * vmax + out32.abs() * 2.0 ** -8 + 1e-5
-    assert bool((d <= bound).all()), f"split vs unsplit {d.max().item():.3e}"
-    assert torch.allclose(lse32, lse, rtol=1e-5, atol=1e-4)
+    o_split = out32.reshape(-1, D).cpu().numpy().astype(np.float64)
+    o_unsplit = o1.reshape(-1, D).cpu().numpy().astype(np.float64)
+    E = _weighted_abs_v(q, k, v, causal=True)
+    bound = (2 * 2.0 ** -8 + 2.0 ** -14) * E + 1e-6
+    d = np.abs(o_split - o_unsplit)
+    ratio = float((d / bound).max())
+    assert ratio <= 1.0, f"split vs unsplit {d.max():.3e}; worst element at {ratio:.2f} of its bound"
+    if P == 1:
+        assert d.max() == 0.0, "one partition is the unsplit computation"
+    _report(f"square_causal_split_vs_unsplit_P{P}", max_abs_diff=float(d.max()), worst_fraction_of_bound=ratio,
+            median_bound=float(np.median(bound)))
+    lse_split = lse32.reshape(-1).cpu().numpy().astype(np.float64)
+    lse_unsplit = l1.reshape(-1).cpu().numpy().astype(np.float64) * math.log(2.0)
+    np.testing.assert_allclose(lse_split, lse_unsplit, rtol=1e-5, atol=1e-4)
     ref, ref_lse = oracle.attn_dense(q, k, v, causal=True)
     _compare(out32.reshape(-1, D), lse32.reshape(-1), ref, ref_lse, "bf16", f"split P={P}")
     _compare(out.reshape(-1, D), lse.reshape(-1), ref, ref_lse, "bf16", "unsplit")
@@ -378,10 +516,8 @@ def test_masked_long_context_full_size(sa):
     l = lse.reshape(N, H)[torch.from_numpy(empty).to(DEV)]
     assert bool((o == 0).all()) and bool((l == -math.inf).all())
     assert bool(torch.isfinite(lse.reshape(N, H)[torch.from_numpy(np.nonzero(vis_any)[0]).to(DEV)]).all())
-    rows = _sample_rows(si.rng_for(87, 0), 1, N, H, 96, extra_rows=(int(empty[0]), 1, 16383))
-    ref, ref_lse = oracle.attn_dense(q, k, v, causal=True, mask=mask, rows=rows)
-    rt = torch.from_numpy(rows).to(DEV)
-    _compare(out.reshape(-1, s["D"])[rt], lse.reshape(-1)[rt], ref, ref_lse, "bf16", "masked")
+    _full_compare(out, lse, q, k, v, "bf16", "masked_B1H16N16384D256_causal_and_mask_all_rows", causal=True,
+                  mask=mask, chunk=1 << 15)
 
 
 def test_long_sequence_mask_past_32_bit_offsets(sa):
