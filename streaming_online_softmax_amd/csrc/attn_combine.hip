@@ -1,16 +1,20 @@
 // attn_combine.hip -- LSE-weighted merge of a split-K workspace (Modular MAX
 // "fa4_splitk_combine": per-row-head formulas, base 2 throughout, and its performance
 // structure), written for wave64:
-//   * one wave per output row-head, four row-heads per workgroup (fewer, larger workgroups to
-//     dispatch); the row's depth is split into 16-byte lane slices, and 64 / (depth/4)
-//     partitions are folded concurrently by separate lane groups;
+//   * one wave per output row-head (four per workgroup when there are many row-heads, one when
+//     there are few, so that a small merge spreads over more compute units); the row's depth is
+//     split into 16-byte lane slices, and 64 / (depth/4) partitions are folded side by side by
+//     separate lane groups;
 //   * the LSE reduction (max, log-sum-exp, per-partition scale) is computed once into lane
 //     registers: lane t holds partitions t, t+64, ...;
-//   * each partition's scale reaches its lane group by a cross-lane read (ds_bpermute) for the
-//     unrolled small-P instantiations, or from a 256-entry LDS table for the runtime-P one;
-//   * loads run ahead of the FMAs: for the unrolled P every slice of the row-head is loaded
-//     before the first is folded; for the runtime P the next slices are loaded before the
-//     current ones are folded (software pipelining), so load latency overlaps the FMAs.
+//   * each partition's scale reaches its lane group by a cross-lane read (ds_bpermute) when
+//     P <= 64, or from a 256-entry LDS table beyond;
+//   * loads run ahead of the arithmetic: the first chunk of slices (16 per lane group) is issued
+//     before the LSE loads, so their two memory round trips overlap, and every further chunk is
+//     issued before the previous one is folded.  P up to 64 runs the instantiation of the next
+//     power of two at or above it (4, 8, 16, 32, 64) with loads past P predicated off, so an
+//     off-rung P such as 37 keeps the unrolled structure; larger P takes the same chunked loop
+//     with a run-time trip count.
 // An empty partition (lse = -inf) gets scale exactly 0; if every partition is empty the output
 // is 0 and the LSE -inf (the all-masked convention of Tylo.jl "Register fragments and logical
 // axes", section "Worked softmax", applied to the merge).
@@ -36,30 +40,48 @@ template <> struct out_store<f16_t> {
   }
 };
 
-constexpr int kCombineWaves = 4;   // row-heads (waves) per workgroup
-
 // The workspace is read exactly once: non-temporal (streaming) loads keep it from displacing
 // other lines in the caches.
 __device__ __forceinline__ f32x4 ld_stream(const float* a) {
   return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a));
 }
 
-template <int P_STATIC, int DEPTH, typename TO>
-__global__ __launch_bounds__(64 * kCombineWaves) void attn_combine_kernel(CombineParams p) {
-  constexpr int LPP = DEPTH / 4;              // lanes per partition slice (16 bytes each)
-  constexpr int G = 64 / LPP;                 // partitions folded at once
-  constexpr int NL = P_STATIC ? (P_STATIC + 63) / 64 : ATTN_P_MAX_DEV / 64;
-  const int P = P_STATIC ? P_STATIC : p.P;
+constexpr int kCombineChunk = 16;   // slices per lane group per chunk of loads
 
-  __shared__ float sc_lds[P_STATIC ? 1 : kCombineWaves][P_STATIC ? 1 : ATTN_P_MAX_DEV];
+// RUNG: the instantiation serves 1 <= P <= RUNG (RUNG = 4, 8, 16, 32 or 64), or any P up to
+// ATTN_P_MAX_DEV when RUNG = 0.  WAVES row-heads (one per wave) per workgroup.
+template <int RUNG, int DEPTH, typename TO, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void attn_combine_kernel(CombineParams p) {
+  constexpr int LPP = DEPTH / 4;              // lanes per partition slice (16 bytes each)
+  constexpr int G = 64 / LPP;                 // partitions folded side by side
+  constexpr int NL = RUNG ? (RUNG + 63) / 64 : ATTN_P_MAX_DEV / 64;   // LSE registers per lane
+  constexpr int NS = RUNG ? (RUNG + G - 1) / G : 0;                  // slices per lane group
+  constexpr int CHS = (RUNG && NS < kCombineChunk) ? NS : kCombineChunk;   // slices per chunk
+  constexpr bool SHFL = RUNG != 0 && RUNG <= 64;   // partition pp's scale sits in lane pp
+  const int P = p.P;
+
+  __shared__ float sc_lds[SHFL ? 1 : WAVES][SHFL ? 1 : ATTN_P_MAX_DEV];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t RH = p.RH;
-  // a wave past the last row-head computes on row-head RH-1 and stores nothing (it still
-  // reaches the workgroup barrier of the runtime-P path)
-  const int64_t rh_w = (int64_t)blockIdx.x * kCombineWaves + wave;
+  // a wave past the last row-head computes on row-head RH-1 and stores nothing
+  const int64_t rh_w = (int64_t)blockIdx.x * WAVES + wave;
   const bool live = rh_w < RH;
   const int64_t rh = live ? rh_w : RH - 1;
+
+  const int g = lane / LPP, dl = lane % LPP;
+  const int64_t pstride = RH * DEPTH;
+  const float* src = p.o_partial + rh * DEPTH + dl * 4;
+  // slice i of chunk c of this lane group holds partition (c * CHS + i) * G + g
+  auto load_chunk = [&](int c, f32x4 (&buf)[CHS]) {
+#pragma unroll
+    for (int i = 0; i < CHS; ++i) {
+      const int pp = (c * CHS + i) * G + g;
+      buf[i] = pp < P ? ld_stream(src + (int64_t)pp * pstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  f32x4 buf_a[CHS], buf_b[CHS];
+  load_chunk(0, buf_a);   // in flight during the LSE phase
 
   // ---- LSE phase: once per row-head, into registers
   float ls[NL];
@@ -81,47 +103,44 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine_kernel(Combin
   float sc[NL];
 #pragma unroll
   for (int t = 0; t < NL; ++t) sc[t] = (empty || ls[t] == kNegInf) ? 0.f : fast_exp2(ls[t] - Gl);
-  if constexpr (!P_STATIC) {
+  if constexpr (!SHFL) {
+    // the wave writes and then reads its own row of the table: LDS operations of one wave
+    // complete in order, so only the compiler must keep the reads after the writes
 #pragma unroll
     for (int t = 0; t < NL; ++t) sc_lds[wave][lane + 64 * t] = sc[t];
-    __syncthreads();   // orders each wave's table writes before its reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-
-  // ---- weighted accumulation over partitions, next slice prefetched
-  const int g = lane / LPP, dl = lane % LPP;
-  const int64_t pstride = RH * DEPTH;
-  const float* src = p.o_partial + rh * DEPTH + dl * 4;
   auto scale_of = [&](int pp) -> float {
-    if constexpr (P_STATIC) {
-      // pp < P_STATIC <= 64: partition pp lives in lane pp, register 0
-      return __shfl(sc[0], pp < P ? pp : 0, 64) * (pp < P ? 1.f : 0.f);
-    } else {
-      return pp < P ? sc_lds[wave][pp] : 0.f;
+    if constexpr (SHFL) return __shfl(sc[0], pp < P ? pp : 0, 64) * (pp < P ? 1.f : 0.f);
+    else return pp < P ? sc_lds[wave][pp] : 0.f;
+  };
+
+  // ---- weighted accumulation over the partitions, one chunk of slices ahead
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto fold_chunk = [&](int c, const f32x4 (&buf)[CHS]) {
+#pragma unroll
+    for (int i = 0; i < CHS; ++i) {
+      const float s = scale_of((c * CHS + i) * G + g);
+      acc += (s != 0.f) ? s * buf[i] : f32x4{0.f, 0.f, 0.f, 0.f};   // an empty partition adds nothing
     }
   };
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (P_STATIC) {
-    constexpr int NS = (P_STATIC + G - 1) / G;   // slices per lane group
-    f32x4 slice[NS];
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int pp = i * G + g;
-      slice[i] = pp < P ? ld_stream(src + (int64_t)pp * pstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+  auto two_chunks = [&](int c, int nch) {
+    if (c + 1 < nch) load_chunk(c + 1, buf_b);
+    fold_chunk(c, buf_a);
+    if (c + 1 < nch) {
+      if (c + 2 < nch) load_chunk(c + 2, buf_a);
+      fold_chunk(c + 1, buf_b);
     }
+  };
+  if constexpr (RUNG != 0) {
+    constexpr int NCH = (NS + CHS - 1) / CHS;
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const float s = scale_of(i * G + g);
-      acc += (s != 0.f) ? s * slice[i] : f32x4{0.f, 0.f, 0.f, 0.f};   // an empty partition adds nothing
-    }
+    for (int c = 0; c < NCH; c += 2) two_chunks(c, NCH);
   } else {
-    f32x4 cur = g < P ? ld_stream(src + (int64_t)g * pstride) : f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int pp0 = 0; pp0 < P; pp0 += G) {
-      const int pn = pp0 + G + g;
-      f32x4 nxt = pn < P ? ld_stream(src + (int64_t)pn * pstride) : f32x4{0.f, 0.f, 0.f, 0.f};
-      const float s = scale_of(pp0 + g);
-      acc += (s != 0.f) ? s * cur : f32x4{0.f, 0.f, 0.f, 0.f};   // an empty partition adds nothing
-      cur = nxt;
-    }
+    const int nch = ((P + G - 1) / G + CHS - 1) / CHS;
+    for (int c = 0; c < nch; c += 2) two_chunks(c, nch);
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = across_groups_sum<LPP>(acc[j]);
@@ -129,24 +148,34 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine_kernel(Combin
   if (live && lane == 0 && p.lse_out) p.lse_out[rh] = empty ? kNegInf : Gl * kLn2;
 }
 
-template <int P_STATIC, int DEPTH>
+// Row-heads per workgroup: four when there are enough row-heads to give every compute unit
+// several workgroups, else one (a decode-sized merge then reaches four times as many units).
+constexpr int64_t kCombineManyRH = 4 * 1024;
+
+template <int RUNG, int DEPTH, typename TO>
+static void launch_combine_w(const CombineParams& p, hipStream_t s) {
+  if (p.RH >= kCombineManyRH)
+    hipLaunchKernelGGL((attn_combine_kernel<RUNG, DEPTH, TO, 4>), dim3((unsigned)((p.RH + 3) / 4)), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<RUNG, DEPTH, TO, 1>), dim3((unsigned)p.RH), dim3(64), 0, s, p);
+}
+
+template <int RUNG, int DEPTH>
 static hipError_t launch_combine_t(const CombineParams& p, int out_dtype, hipStream_t s) {
-  dim3 grid((unsigned)((p.RH + kCombineWaves - 1) / kCombineWaves));
-  dim3 block(64 * kCombineWaves);
-  if (out_dtype == 2) hipLaunchKernelGGL((attn_combine_kernel<P_STATIC, DEPTH, float>), grid, block, 0, s, p);
-  else if (out_dtype == 0) hipLaunchKernelGGL((attn_combine_kernel<P_STATIC, DEPTH, bf16_t>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((attn_combine_kernel<P_STATIC, DEPTH, f16_t>), grid, block, 0, s, p);
+  if (out_dtype == 2) launch_combine_w<RUNG, DEPTH, float>(p, s);
+  else if (out_dtype == 0) launch_combine_w<RUNG, DEPTH, bf16_t>(p, s);
+  else launch_combine_w<RUNG, DEPTH, f16_t>(p, s);
   return hipGetLastError();
 }
 
 template <int DEPTH>
 static hipError_t launch_combine_depth(const CombineParams& p, int out_dtype, hipStream_t s) {
-  switch (p.P) {
-    case 4: return launch_combine_t<4, DEPTH>(p, out_dtype, s);
-    case 8: return launch_combine_t<8, DEPTH>(p, out_dtype, s);
-    case 16: return launch_combine_t<16, DEPTH>(p, out_dtype, s);
-    default: return launch_combine_t<0, DEPTH>(p, out_dtype, s);
-  }
+  if (p.P <= 4) return launch_combine_t<4, DEPTH>(p, out_dtype, s);
+  if (p.P <= 8) return launch_combine_t<8, DEPTH>(p, out_dtype, s);
+  if (p.P <= 16) return launch_combine_t<16, DEPTH>(p, out_dtype, s);
+  if (p.P <= 32) return launch_combine_t<32, DEPTH>(p, out_dtype, s);
+  if (p.P <= 64) return launch_combine_t<64, DEPTH>(p, out_dtype, s);
+  return launch_combine_t<0, DEPTH>(p, out_dtype, s);
 }
 
 hipError_t launch_combine(const CombineParams& p, int depth, int out_dtype, hipStream_t s) {
