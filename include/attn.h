@@ -17,6 +17,8 @@
  *                    "fa4_splitk_combine", per-row-head formulas (base 2 throughout).
  *   attn_fwd_splitk_fused   attn_fwd_splitk and attn_combine in one launch (the last
  *                    workgroup of each row-head merges).
+ *   attn_fwd_splitk_noalloc  attn_fwd_splitk and attn_combine with the workspace in the
+ *                    library's static device memory, for callers that cannot allocate.
  *   attn_softmax_rows        standalone row softmax (streaming, registers or three-pass)
  *                    with the all-masked conventions of Tylo.jl "Register fragments and
  *                    logical axes", section "Worked softmax".
@@ -27,7 +29,8 @@
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library allocates
- *     nothing, keeps no state between calls and may be called from several threads at once.
+ *     nothing, keeps no state between calls and may be called from several threads at once
+ *     (attn_fwd_splitk_noalloc excepted: it keeps its workspace in the library; see there).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous: ATTN_OK
  *     means "arguments valid, kernels enqueued".  A fault inside a kernel surfaces at the
  *     caller's next synchronisation on that stream.
@@ -61,6 +64,7 @@ extern "C" {
 #define ATTN_ABI_VERSION 1
 #define ATTN_P_MAX 256 /* largest split count: one partition per MI355X compute unit */
 #define ATTN_TICKET_STRIDE 32 /* uint32 slots per row-head in a fused-decode ticket array (128 B) */
+#define ATTN_NOALLOC_SCRATCH_BYTES (64u << 20) /* per-GPU workspace of attn_fwd_splitk_noalloc */
 
 enum attn_dtype {
   ATTN_BF16 = 0,
@@ -113,6 +117,30 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
 int attn_fwd_splitk(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
                     int Nq, int Nkv, int D, int causal, const uint8_t* mask, int P, float* o_partial,
                     float* lse_partial, int dtype, void* stream);
+
+/*
+ * attn_fwd_splitk_noalloc -- attn_fwd_splitk with out != NULL (the split-K producer, then the
+ *   combine, on the same kernels), for callers that cannot allocate device memory: code under
+ *   HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The call allocates
+ *   and frees nothing (no hipMalloc, hipFree or allocating library routine): the workspace
+ *   (o_partial [P, B*Nq, H, D] float32, then lse_partial [P, B*Nq, H] float32 at the next
+ *   256-byte boundary) lives in a static device array of ATTN_NOALLOC_SCRATCH_BYTES inside the
+ *   library, one per GPU, held until the process ends; its address is looked up on the first call
+ *   on each device.
+ *   Arguments: as attn_fwd_splitk without o_partial and lse_partial; out is REQUIRED.
+ *   Limit: P * B * Nq * H * D * 4, rounded up to 256, plus P * B * Nq * H * 4 must not exceed
+ *   ATTN_NOALLOC_SCRATCH_BYTES (64 MiB: the decode shape B8 H32 D128 fits up to P = 256),
+ *   else ATTN_E_WORKSPACE and nothing is enqueued.
+ *   Sharing: every call on one GPU uses that GPU's array, which keeps the last call's contents.
+ *   Each call writes every workspace entry before its combine reads it, so nothing needs
+ *   clearing, but calls that overlap in time on one GPU (other streams, other host threads)
+ *   race on the array: the caller must order them.  `stream` must belong to the current device
+ *   (ATTN_E_HIP otherwise).
+ *   Errors: those of attn_fwd_splitk and attn_combine, plus ATTN_E_WORKSPACE for the limit.
+ */
+int attn_fwd_splitk_noalloc(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                            int Nq, int Nkv, int D, int causal, const uint8_t* mask, int P, int dtype,
+                            void* stream);
 
 /*
  * attn_fwd_splitk_fused -- attn_fwd_splitk followed by the combine, in ONE launch (the CDNA4

@@ -10,6 +10,8 @@ Entry points (same names as the C ABI in include/attn.h):
                     mask=None, stream=None)
     attn_fwd_splitk_fused(q, k, v, P, o_partial, lse_partial, tickets, out, lse=None, causal=False,
                           mask=None, stream=None)
+    attn_fwd_splitk_noalloc(q, k, v, P, out, lse=None, causal=False, mask=None, stream=None)
+                    (the workspace in the library's static device memory; nothing allocated)
     attn_combine(o_partial, lse_partial, out, lse_out=None, stream=None)
     attn_softmax_rows(x, y, method=SOFTMAX_STREAMING, stream=None)   (x, y: [..., n])
     attn_fwd_fp8v(q, k, v, v_scale, out, lse=None, causal=False, mask=None, v_format=None, stream=None)
@@ -35,6 +37,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_E_NULL", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUPPOR
           4: "ATTN_E_ALIGN", 5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
 P_MAX = 256
 TICKET_STRIDE = 32          # int32 slots per row-head in a fused-decode ticket array
+NOALLOC_SCRATCH_BYTES = 64 << 20   # per-GPU static workspace of attn_fwd_splitk_noalloc
 SOFTMAX_STREAMING, SOFTMAX_REGISTERS, SOFTMAX_THREE_PASS = 0, 1, 2
 
 
@@ -73,6 +76,8 @@ def _load():
     L.attn_fwd_splitk.restype = i32
     L.attn_fwd_splitk_fused.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp, vp, vp, i32, vp]
     L.attn_fwd_splitk_fused.restype = i32
+    L.attn_fwd_splitk_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, i32, vp]
+    L.attn_fwd_splitk_noalloc.restype = i32
     L.attn_softmax_rows.argtypes = [vp, vp, ctypes.c_int64, i32, i32, i32, vp]
     L.attn_softmax_rows.restype = i32
     L.attn_round.argtypes = [vp, vp, ctypes.c_int64, i32, vp]
@@ -155,6 +160,15 @@ def attn_fwd_splitk_fused(q, k, v, P, o_partial, lse_partial, tickets, out, lse=
     _check(lib().attn_fwd_splitk_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nkv, D,
                                      int(causal), _ptr(mask), int(P), _ptr(o_partial), _ptr(lse_partial),
                                      _ptr(tickets), _dtype_code(q), _stream(stream)))
+
+
+def attn_fwd_splitk_noalloc(q, k, v, P, out, lse=None, causal=False, mask=None, stream=None):
+    """attn_fwd_splitk with the combine, its workspace in the library's static device array
+    (no allocation on any path; calls that overlap on one GPU race on that array)."""
+    B, Nq, H, D = q.shape
+    Nkv = k.shape[1]
+    _check(lib().attn_fwd_splitk_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nkv, D,
+                                         int(causal), _ptr(mask), int(P), _dtype_code(q), _stream(stream)))
 
 
 def attn_combine(o_partial, lse_partial, out, lse_out=None, stream=None):

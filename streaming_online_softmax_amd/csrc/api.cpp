@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "../../include/attn.h"
 #include "launch.h"
@@ -59,6 +60,41 @@ int check_qkv(const void* q, const void* k, const void* v, int B, int H, int Nq,
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(ATTN_E_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
+}
+
+// ---- the workspace of attn_fwd_splitk_noalloc: one static device array, which every GPU the
+//      library runs on holds (with the code object) until the process ends.  In host code the
+//      name `scratch` is only a handle for the runtime; the device address comes from
+//      hipGetSymbolAddress, looked up once per device with that device current and kept here.
+constexpr uint64_t kScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the device `stream` runs on, which must be the current device.
+int scratch_for_stream(hipStream_t stream, uint8_t** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_E_HIP, "device ordinal %d out of range", dev);
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+    if (sdev != dev) return fail(ATTN_E_HIP, "the stream belongs to device %d but device %d is current", (int)sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(ATTN_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return ATTN_OK;
 }
 
 int do_combine(const float* o_partial, const float* lse_partial, void* out, float* lse_out, int P,
@@ -115,6 +151,46 @@ int fwd_impl(const attn_fwd_args* a, hipStream_t s) {
   return hip_status(attn::launch_fwd(p, a->dtype, a->D, BN, false, s), "attn_fwd launch");
 }
 
+int splitk_impl(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Nq,
+                int Nkv, int D, int causal, const uint8_t* mask, int P, float* o_partial, float* lse_partial,
+                int dtype, hipStream_t s) {
+  int rc = check_qkv(q, k, v, B, H, Nq, Nkv, D, causal, dtype);
+  if (rc) return rc;
+  if (P < 1) return fail(ATTN_E_SHAPE, "P must be >= 1 (got %d)", P);
+  if (P > ATTN_P_MAX) return fail(ATTN_E_UNSUPPORTED, "P=%d exceeds ATTN_P_MAX=%d", P, ATTN_P_MAX);
+  if (!o_partial || !lse_partial) return fail(ATTN_E_WORKSPACE, "o_partial and lse_partial are required");
+  if (!aligned(o_partial, 16)) return fail(ATTN_E_ALIGN, "o_partial must be 16-byte aligned");
+  if (!aligned(lse_partial, 4)) return fail(ATTN_E_ALIGN, "lse_partial must be 4-byte aligned");
+  const int64_t RH = (int64_t)B * Nq * H;
+  if (RH > 0x7fffffffLL) return fail(ATTN_E_SHAPE, "B*Nq*H exceeds 2^31-1");
+  if (out) {
+    rc = check_combine(o_partial, lse_partial, out, lse, P, B * Nq, H, D, dtype);
+    if (rc) return rc;
+  }
+  const int chunk = (int)(((int64_t)Nkv + P - 1) / P);
+  const float c = scale_log2(D);
+  if (Nq == 1) {
+    if (RH * P > 0x7fffffffLL) return fail(ATTN_E_SHAPE, "grid too large");
+    attn::DecodeParams p{};
+    p.q = q; p.k = k; p.v = v; p.o_partial = o_partial; p.lse_partial = lse_partial; p.mask = mask;
+    p.B = B; p.H = H; p.Nq = Nq; p.Nkv = Nkv; p.causal = causal; p.P = P; p.chunk = chunk; p.scale_log2 = c;
+    rc = hip_status(attn::launch_decode(p, dtype, D, false, s), "attn_fwd_splitk decode launch");
+  } else {
+    const int64_t nqb = ((int64_t)Nq + attn::fwd_block_m() - 1) / attn::fwd_block_m();
+    if (nqb * H * B * P > 0x7fffffffLL) return fail(ATTN_E_SHAPE, "grid too large");
+    attn::FwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.o_partial = o_partial; p.lse_partial = lse_partial; p.mask = mask;
+    p.B = B; p.H = H; p.Nq = Nq; p.Nkv = Nkv; p.causal = causal; p.P = P; p.chunk = chunk;
+    p.n_qblocks = (int)nqb;
+    p.mask_vec = mask && aligned(mask, 8) && (Nkv % 8 == 0) && (chunk % 8 == 0);
+    p.mask_lds = mask && aligned(mask, 16) && (Nkv % 16 == 0) && (chunk % 16 == 0) && ((int64_t)Nq + 256) * Nkv < (1LL << 32);
+    p.scale_log2 = c;
+    rc = hip_status(attn::launch_fwd(p, dtype, D, 64, true, s), "attn_fwd_splitk launch");
+  }
+  if (rc || !out) return rc;
+  return do_combine(o_partial, lse_partial, out, lse, P, B * Nq, H, D, dtype, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -167,42 +243,34 @@ int attn_fwd_fp8v(const void* q, const void* k, const uint8_t* v, int v_format, 
 int attn_fwd_splitk(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
                     int Nq, int Nkv, int D, int causal, const uint8_t* mask, int P, float* o_partial,
                     float* lse_partial, int dtype, void* stream) {
+  return splitk_impl(q, k, v, out, lse, B, H, Nq, Nkv, D, causal, mask, P, o_partial, lse_partial, dtype,
+                     (hipStream_t)stream);
+}
+
+int attn_fwd_splitk_noalloc(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                            int Nq, int Nkv, int D, int causal, const uint8_t* mask, int P, int dtype,
+                            void* stream) {
+  // every argument is checked before the device is touched
   int rc = check_qkv(q, k, v, B, H, Nq, Nkv, D, causal, dtype);
   if (rc) return rc;
   if (P < 1) return fail(ATTN_E_SHAPE, "P must be >= 1 (got %d)", P);
   if (P > ATTN_P_MAX) return fail(ATTN_E_UNSUPPORTED, "P=%d exceeds ATTN_P_MAX=%d", P, ATTN_P_MAX);
-  if (!o_partial || !lse_partial) return fail(ATTN_E_WORKSPACE, "o_partial and lse_partial are required");
-  if (!aligned(o_partial, 16)) return fail(ATTN_E_ALIGN, "o_partial must be 16-byte aligned");
-  if (!aligned(lse_partial, 4)) return fail(ATTN_E_ALIGN, "lse_partial must be 4-byte aligned");
-  const int64_t RH = (int64_t)B * Nq * H;
-  if (RH > 0x7fffffffLL) return fail(ATTN_E_SHAPE, "B*Nq*H exceeds 2^31-1");
-  if (out) {
-    rc = check_combine(o_partial, lse_partial, out, lse, P, B * Nq, H, D, dtype);
-    if (rc) return rc;
-  }
-  const int chunk = (int)(((int64_t)Nkv + P - 1) / P);
-  const float c = scale_log2(D);
-  hipStream_t s = (hipStream_t)stream;
-  if (Nq == 1) {
-    if (RH * P > 0x7fffffffLL) return fail(ATTN_E_SHAPE, "grid too large");
-    attn::DecodeParams p{};
-    p.q = q; p.k = k; p.v = v; p.o_partial = o_partial; p.lse_partial = lse_partial; p.mask = mask;
-    p.B = B; p.H = H; p.Nq = Nq; p.Nkv = Nkv; p.causal = causal; p.P = P; p.chunk = chunk; p.scale_log2 = c;
-    rc = hip_status(attn::launch_decode(p, dtype, D, false, s), "attn_fwd_splitk decode launch");
-  } else {
-    const int64_t nqb = ((int64_t)Nq + attn::fwd_block_m() - 1) / attn::fwd_block_m();
-    if (nqb * H * B * P > 0x7fffffffLL) return fail(ATTN_E_SHAPE, "grid too large");
-    attn::FwdParams p{};
-    p.q = q; p.k = k; p.v = v; p.o_partial = o_partial; p.lse_partial = lse_partial; p.mask = mask;
-    p.B = B; p.H = H; p.Nq = Nq; p.Nkv = Nkv; p.causal = causal; p.P = P; p.chunk = chunk;
-    p.n_qblocks = (int)nqb;
-    p.mask_vec = mask && aligned(mask, 8) && (Nkv % 8 == 0) && (chunk % 8 == 0);
-    p.mask_lds = mask && aligned(mask, 16) && (Nkv % 16 == 0) && (chunk % 16 == 0) && ((int64_t)Nq + 256) * Nkv < (1LL << 32);
-    p.scale_log2 = c;
-    rc = hip_status(attn::launch_fwd(p, dtype, D, 64, true, s), "attn_fwd_splitk launch");
-  }
-  if (rc || !out) return rc;
-  return do_combine(o_partial, lse_partial, out, lse, P, B * Nq, H, D, dtype, s);
+  if (!out) return fail(ATTN_E_NULL, "out is required");
+  if (!aligned(out, 16)) return fail(ATTN_E_ALIGN, "out must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(ATTN_E_ALIGN, "lse must be 4-byte aligned");
+  if ((int64_t)B * Nq * H > 0x7fffffffLL) return fail(ATTN_E_SHAPE, "B*Nq*H exceeds 2^31-1");
+  const uint64_t rh_all = (uint64_t)P * B * Nq * H;
+  const uint64_t o_bytes = (rh_all * D * 4 + 255) / 256 * 256;
+  const uint64_t need = o_bytes + rh_all * 4;
+  if ((double)P * B * Nq * H * (D + 1) * 4.0 > 1.0e15 || need > kScratchBytes)
+    return fail(ATTN_E_WORKSPACE, "workspace of %llu bytes (P*B*Nq*H*(D+1)*4, lse at a 256-byte boundary) exceeds the "
+                "%llu-byte static scratch of attn_fwd_splitk_noalloc", (unsigned long long)need,
+                (unsigned long long)kScratchBytes);
+  uint8_t* ws = nullptr;
+  rc = scratch_for_stream((hipStream_t)stream, &ws);
+  if (rc) return rc;
+  return splitk_impl(q, k, v, out, lse, B, H, Nq, Nkv, D, causal, mask, P, reinterpret_cast<float*>(ws),
+                     reinterpret_cast<float*>(ws + o_bytes), dtype, (hipStream_t)stream);
 }
 
 int attn_fwd_splitk_fused(const void* q, const void* k, const void* v, void* out, float* lse, int B,

@@ -14,7 +14,8 @@ E_NULL, E_SHAPE, E_UNSUP, E_ALIGN, E_WS = 1, 2, 3, 4, 5
 def test_library_exports_every_declared_symbol():
     names = sa.declared_symbols()
     assert {"attn_fwd", "attn_fwd_splitk", "attn_fwd_splitk_fused", "attn_combine", "attn_softmax_rows",
-            "attn_round", "attn_fwd_fp8v", "attn_fwd_ex", "attn_last_error", "attn_abi_version"} <= set(names)
+            "attn_round", "attn_fwd_fp8v", "attn_fwd_ex", "attn_last_error", "attn_abi_version",
+            "attn_fwd_splitk_noalloc"} <= set(names)
     for n in names:
         assert hasattr(sa.lib(), n), n
 
@@ -41,6 +42,7 @@ def test_header_is_plain_c_and_cpp(lang, std, tmp_path):
                        "         attn_fwd(0, 0, 0, 0, 0, 1, 1, 1, 64, 0, 0, ATTN_BF16, 0) == ATTN_E_NULL &&\n"
                        "         attn_fwd_splitk(0, 0, 0, 0, 0, 1, 1, 1, 1, 64, 0, 0, 1, 0, 0, ATTN_BF16, 0) == ATTN_E_NULL &&\n"
                        "         attn_fwd_splitk_fused(0, 0, 0, 0, 0, 1, 1, 1, 1, 64, 0, 0, 1, 0, 0, 0, ATTN_BF16, 0) == ATTN_E_NULL &&\n"
+                       "         attn_fwd_splitk_noalloc(0, 0, 0, 0, 0, 1, 1, 1, 1, 64, 0, 0, 1, ATTN_BF16, 0) == ATTN_E_NULL &&\n"
                        "         attn_combine(0, 0, 0, 0, 1, 1, 1, 64, ATTN_FP32, 0) == ATTN_E_NULL &&\n"
                        "         attn_softmax_rows(0, 0, 1, 1, ATTN_FP32, ATTN_SOFTMAX_STREAMING, 0) == ATTN_E_NULL &&\n"
                        "         attn_fwd_fp8v(0, 0, 0, ATTN_FP8_E4M3, 1.0f, 0, 0, 1, 1, 1, 128, 0, 0, ATTN_BF16, 0) == ATTN_E_NULL &&\n"
@@ -71,6 +73,8 @@ def test_binding_constants_match_the_header():
     assert defines["ATTN_P_MAX"] == sa.P_MAX
     assert defines["ATTN_TICKET_STRIDE"] == sa.TICKET_STRIDE
     assert defines["ATTN_ABI_VERSION"] == sa.attn_abi_version()
+    scratch = re.search(r"^#define ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text, re.M)
+    assert int(scratch.group(1)) << int(scratch.group(2)) == sa.NOALLOC_SCRATCH_BYTES
     for name in ("ATTN_BF16", "ATTN_FP16", "ATTN_FP32", "ATTN_FP8_E4M3", "ATTN_FP8_E5M2",
                  "ATTN_SOFTMAX_STREAMING", "ATTN_SOFTMAX_REGISTERS", "ATTN_SOFTMAX_THREE_PASS"):
         binding = name[len("ATTN_"):] if name.startswith("ATTN_SOFTMAX") else name
@@ -97,6 +101,10 @@ def fused(q=A, k=A, v=A, out=A, lse=None, B=1, H=1, Nq=1, Nkv=64, D=64, causal=0
           o_p=A, l_p=A, tk=A, dtype=0):
     return sa.lib().attn_fwd_splitk_fused(q, k, v, out, lse, B, H, Nq, Nkv, D, causal, mask, P, o_p, l_p, tk,
                                           dtype, None)
+
+
+def noalloc(q=A, k=A, v=A, out=A, lse=None, B=1, H=1, Nq=1, Nkv=64, D=64, causal=0, mask=None, P=4, dtype=0):
+    return sa.lib().attn_fwd_splitk_noalloc(q, k, v, out, lse, B, H, Nq, Nkv, D, causal, mask, P, dtype, None)
 
 
 def softmax(x=A, y=A, rows=1, n=64, dtype=2, method=0):
@@ -141,6 +149,17 @@ def combine(o_p=A, l_p=A, out=A, lse=None, P=4, rows=1, heads=1, depth=64, out_d
     (lambda: fused(tk=A + 2), E_ALIGN),
     (lambda: fused(P=300), E_UNSUP),
     (lambda: fused(causal=1), E_SHAPE),
+    (lambda: noalloc(q=None), E_NULL),
+    (lambda: noalloc(out=None), E_NULL),
+    (lambda: noalloc(out=BAD), E_ALIGN),
+    (lambda: noalloc(lse=A + 2), E_ALIGN),
+    (lambda: noalloc(P=0), E_SHAPE),
+    (lambda: noalloc(P=257), E_UNSUP),
+    (lambda: noalloc(causal=1), E_SHAPE),
+    (lambda: noalloc(D=48), E_UNSUP),
+    # 256 * 300 * 256 * 4 B of o_partial = 78.6 MB > the 64 MiB scratch; then the smallest Nq past it
+    (lambda: noalloc(P=256, H=300, D=256), E_WS),
+    (lambda: noalloc(P=256, H=1, Nq=(64 << 20) // (256 * 129 * 4) + 1, D=128), E_WS),
     (lambda: softmax(x=None), E_NULL),
     (lambda: softmax(rows=0), E_SHAPE),
     (lambda: softmax(n=0), E_SHAPE),
