@@ -157,8 +157,9 @@ void oracle_round_array(const float* x, int64_t n, int target_dtype, uint16_t* o
 
 /* ---------------------------------------------------------------------------------------------
  * O6. Round-to-nearest-even conversion of a float32 to E4M3 / E5M2 bits with saturation to the
- * largest finite value ([TR] Logical types and register packing: the 8-bit float types convert
- * from FP32 to nearest even and saturate to the largest finite value).  Same construction as
+ * largest finite value ([TR] Logical types and register packing: FP32 values are converted to the
+ * two 8-bit formats by nearest-even rounding, and magnitudes past the format's range are clamped
+ * to its largest finite value rather than becoming infinite).  Same construction as
  * O4: the two neighbouring values at the input's binade spacing (exponent range unbounded
  * above), the nearer, ties to the even last significand bit; a result beyond the largest finite
  * value (448 for E4M3, 57344 for E5M2), and an infinite input, become that value with the
@@ -256,8 +257,8 @@ static void rh_split(int64_t rh, int Nq, int H, int* b, int* i, int* h) {
 
 /* ---------------------------------------------------------------------------------------------
  * O1. Dense definition of attention for the selected row-heads.
- *   vis(i) = visible keys.  If vis(i) is empty: O_i = 0, LSE_i = -inf ([TS] Online statistics:
- *   entirely masked rows normalize to zero and have log-sum-exp -Inf; [TR] Worked softmax).
+ *   vis(i) = visible keys.  If vis(i) is empty: O_i = 0, LSE_i = -inf ([TS] Online statistics and
+ *   [TR] Worked softmax: a row with every key masked yields zeros and a log-sum-exp of -inf).
  *   Otherwise M = max_j s_ij, w_j = exp(s_ij - M), L = sum w_j, O_i = sum_j w_j v_j / L and
  *   LSE_i = M + ln L (natural log).
  * sel: row-head indices (NULL = all B*Nq*H in order).  out: [nsel, D]; lse: [nsel] (nullable).
@@ -305,53 +306,79 @@ int oracle_attn_dense(const void* q, const void* k, const void* v, int dt, const
 }
 
 /* ---------------------------------------------------------------------------------------------
- * O2. The chunked online recurrence over BN-key tiles, in the order the workshop's loop states
- * it ([WS] Keep three quantities for each query row), with the empty state (-inf, 0) and the
- * guards that keep an all-masked tile from producing -inf - (-inf) ([TS] Online statistics;
- * [TR] Worked softmax: shift_logit / normalize_weight):
- *     m' = max(m, max_j s_j);   m_use = (m' == -inf) ? 0 : m'
- *     alpha = exp(m - m_use);   p_j = exp(s_j - m_use)   (masked s_j = -inf gives p_j = 0)
- *     l = alpha*l + sum_j p_j;  a = alpha*a + sum_j p_j v_j;  m = m'
- *   finish: O = (l == 0) ? 0 : a / l;  LSE = (l == 0) ? -inf : m + ln l.
- * flags: OR_NO_NUMERATOR_RESCALE drops the alpha on a (the bug the trace exposes, which gives 7
- * instead of 6); OR_SAME_BOUNDARY_* rounds p_j to bf16/f16 before p_j v_j while l keeps the
- * unrounded p_j ([TS] Attention as a consumer: probability rounding before PV, FP32
- * denominator).  tile_trace (nullable) receives (m, l, a[0], alpha) after every tile.
+ * O2. The online recurrence over BN-key tiles ([WS] Keep three quantities for each query row;
+ * [TS] Online statistics for the empty state and the guards; [TR] Worked softmax).
+ *
+ * A query row carries a summary of the keys absorbed so far: the reference m (their largest
+ * logit, -inf before any visible key), l (the sum of their exponentials taken against m) and
+ * a[D] (the same exponentials weighting their value rows).  A tile is absorbed in the order the
+ * workshop gives: the reference moves to the larger of m and the tile's largest logit; the old
+ * l and a, expressed against the old reference, shrink by exp(old - new) (0 for the empty
+ * summary); the tile's exponentials against the new reference are added to l, and their
+ * value-weighted sums to a.  While the reference is still -inf the exponentials are taken
+ * against 0, so no -inf - (-inf) arises and a masked logit (-inf) weighs exactly 0.  Finally
+ * O = a / l and LSE = m + ln l, or 0 and -inf when nothing was visible (l = 0).
+ *
+ * flags: OR_NO_NUMERATOR_RESCALE keeps a unshrunk when the reference moves (the mistake the
+ * worked trace exposes, which turns its 6 into 7); OR_SAME_BOUNDARY_* rounds each weight to bf16
+ * / f16 before it multiplies its value row, while l takes the weight unrounded ([TS] Attention as
+ * a consumer).  tile_trace (nullable) receives (m, l, a[0], shrink factor) after every tile.
  * ------------------------------------------------------------------------------------------- */
+typedef struct {
+  double m;    /* reference: the largest logit absorbed (-inf: none visible yet) */
+  double l;    /* sum over absorbed keys of exp(logit - m) */
+  double* a;   /* sum over absorbed keys of exp(logit - m) * value row (D entries) */
+} row_state_t;
+
+/* Absorbs keys j0 .. j1-1 (logits s, value rows vrows[j*D ..]) into st; w holds j1 - j0 doubles
+ * of scratch.  Returns the factor the previous l and a were scaled by. */
+static double absorb_tile(row_state_t* st, const double* s, const double* vrows, int j0, int j1, int D,
+                          int flags, double* w) {
+  double ref = st->m;
+  for (int j = j0; j < j1; ++j)
+    if (s[j] > ref) ref = s[j];
+  const double base = (ref == -INFINITY) ? 0.0 : ref;
+  const double shrink = exp(st->m - base);
+  double tile_l = 0.0;
+  for (int j = j0; j < j1; ++j) {
+    w[j - j0] = exp(s[j] - base);
+    tile_l += w[j - j0];
+  }
+  st->l = shrink * st->l + tile_l;
+  const double keep = (flags & OR_NO_NUMERATOR_RESCALE) ? 1.0 : shrink;
+  const int rounded = flags & (OR_SAME_BOUNDARY_BF16 | OR_SAME_BOUNDARY_F16);
+  for (int d = 0; d < D; ++d) {
+    double acc = keep * st->a[d];
+    for (int j = j0; j < j1; ++j) {
+      const double wj = rounded ? round_value((float)w[j - j0], flags) : w[j - j0];
+      acc += wj * vrows[(int64_t)j * D + d];
+    }
+    st->a[d] = acc;
+  }
+  st->m = ref;
+  return shrink;
+}
+
 static void online_core(const double* s, const double* vrows, int n, int D, int BN, int flags,
                         double* o, double* lse, double* tile_trace) {
-  double m = -INFINITY, l = 0.0;
-  double* a = (double*)calloc((size_t)D, sizeof(double));
+  row_state_t st = {-INFINITY, 0.0, (double*)calloc((size_t)(D > 0 ? D : 1), sizeof(double))};
+  double* w = (double*)malloc(sizeof(double) * (size_t)(BN > 0 ? BN : 1));
   int tile = 0;
   for (int j0 = 0; j0 < n; j0 += BN, ++tile) {
-    int j1 = j0 + BN < n ? j0 + BN : n;
-    double mx = -INFINITY;
-    for (int j = j0; j < j1; ++j) if (s[j] > mx) mx = s[j];
-    double m_new = m > mx ? m : mx;
-    double m_use = (m_new == -INFINITY) ? 0.0 : m_new;
-    double alpha = exp(m - m_use);
-    double psum = 0.0;
-    l *= alpha;
-    if (!(flags & OR_NO_NUMERATOR_RESCALE))
-      for (int d = 0; d < D; ++d) a[d] *= alpha;
-    for (int j = j0; j < j1; ++j) {
-      double p = exp(s[j] - m_use);
-      psum += p;
-      double pv = (flags & (OR_SAME_BOUNDARY_BF16 | OR_SAME_BOUNDARY_F16)) ? round_value((float)p, flags) : p;
-      for (int d = 0; d < D; ++d) a[d] += pv * vrows[(int64_t)j * D + d];
-    }
-    l += psum;
-    m = m_new;
+    const double shrink = absorb_tile(&st, s, vrows, j0, j0 + BN < n ? j0 + BN : n, D, flags, w);
     if (tile_trace) {
-      tile_trace[4 * tile + 0] = m;
-      tile_trace[4 * tile + 1] = l;
-      tile_trace[4 * tile + 2] = a[0];
-      tile_trace[4 * tile + 3] = alpha;
+      double* t = tile_trace + 4 * tile;
+      t[0] = st.m;
+      t[1] = st.l;
+      t[2] = st.a[0];
+      t[3] = shrink;
     }
   }
-  for (int d = 0; d < D; ++d) o[d] = (l == 0.0) ? 0.0 : a[d] / l;
-  if (lse) *lse = (l == 0.0) ? -INFINITY : m + log(l);
-  free(a);
+  const int seen = st.l != 0.0;
+  for (int d = 0; d < D; ++d) o[d] = seen ? st.a[d] / st.l : 0.0;
+  if (lse) *lse = seen ? st.m + log(st.l) : -INFINITY;
+  free(w);
+  free(st.a);
 }
 
 /* Logits-in entry point for the worked trace: s[n] are already-scaled logits (-inf = masked),
@@ -490,30 +517,33 @@ int oracle_splitk(const void* q, const void* k, const void* v, int dt, const uin
 }
 
 /* ---------------------------------------------------------------------------------------------
- * O5. Row softmax with the all-masked conventions ([TR] "Worked softmax"): per row of n logits
- *   m = max_j x_j;  shift(x, m) = (m == -inf) ? -inf : x - m;  w_j = exp(shift(x_j, m));
- *   s = sum_j w_j;  y_j = (s == 0) ? 0 : w_j / s.
- * A logit of -inf is a masked entry (weight 0); a row of only -inf gives all zeros.  x is a
- * row-major [rows, n] array of float32, bfloat16 or float16; y is [rows, n] double.
+ * O5. Row softmax with the all-masked convention ([TR] "Worked softmax"; [TS] Online statistics):
+ * for each row of n logits, y_j = exp(x_j - M) / sum_k exp(x_k - M) with M the row maximum.  A
+ * logit of -inf is a masked entry and gets weight 0.  A row whose entries are all -inf has no
+ * finite maximum; subtracting it would give -inf - (-inf), so such a row is defined as all zeros
+ * and handled before any subtraction.  Otherwise the entry equal to M contributes exp(0) = 1, so
+ * the sum is at least 1 and the division is safe.  x is a row-major [rows, n] array of float32,
+ * bfloat16 or float16; y is [rows, n] double.
  * ------------------------------------------------------------------------------------------- */
-static double shift_logit(double x, double m) { return m == -INFINITY ? -INFINITY : x - m; }
-static double normalize_weight(double w, double s) { return s == 0.0 ? 0.0 : w / s; }
-
 void oracle_softmax_rows(const void* x, int dtype, int64_t rows, int64_t n, double* y) {
 #pragma omp parallel for schedule(dynamic, 16)
   for (int64_t r = 0; r < rows; ++r) {
-    double m = -INFINITY;
+    double* yr = y + r * n;
+    double top = -INFINITY;
     for (int64_t j = 0; j < n; ++j) {
-      double v = load_elem(x, r * n + j, dtype);
-      if (v > m) m = v;
+      const double v = load_elem(x, r * n + j, dtype);
+      if (v > top) top = v;
     }
-    double s = 0.0;
+    if (top == -INFINITY) {                 /* every entry masked */
+      for (int64_t j = 0; j < n; ++j) yr[j] = 0.0;
+      continue;
+    }
+    double total = 0.0;
     for (int64_t j = 0; j < n; ++j) {
-      double w = exp(shift_logit(load_elem(x, r * n + j, dtype), m));
-      y[r * n + j] = w;
-      s += w;
+      yr[j] = exp(load_elem(x, r * n + j, dtype) - top);   /* -inf entries give 0 */
+      total += yr[j];
     }
-    for (int64_t j = 0; j < n; ++j) y[r * n + j] = normalize_weight(y[r * n + j], s);
+    for (int64_t j = 0; j < n; ++j) yr[j] /= total;
   }
 }
 

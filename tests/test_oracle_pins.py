@@ -59,7 +59,8 @@ def test_worked_trace_bug_gives_seven():
 
 
 def test_worked_trace_dense_and_weights():
-    """Same passage: the full softmax weights [1/4, 1/4, 1/2] give the same 6.  The dense
+    """Same passage: softmax over all three logits at once weighs the keys 1/4, 1/4 and 1/2, and
+    the weighted value is again 6.  The dense
     definition is fed D=1, q=1, k = logits so that q.k/sqrt(1) reproduces the logits; the
     weights are read out by giving V the identity rows."""
     g = _golden("worked_trace.json")
@@ -451,7 +452,7 @@ def test_decode_every_pattern():
 
 # ------------------------------------------------------------------------------------------
 # O6: 8-bit floats (Tylo "Register fragments and logical axes", "Logical types and register
-# packing": Float8E4M3 / Float8E5M2, round to nearest even, saturate to the largest finite value)
+# packing": Float8E4M3 / Float8E5M2, nearest even rounding, out-of-range results clamped to the largest finite value)
 # ------------------------------------------------------------------------------------------
 _TORCH_FP8 = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
 _FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
