@@ -20,7 +20,7 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int BN, bool split, 
   return dtype == 0 ? launch_fwd_dtype<bf16_t>(p, D, BN, split, s) : launch_fwd_dtype<f16_t>(p, D, BN, split, s);
 }
 
-template <typename T, bool MASK, int FMT>
+template <typename T, int MASK, int FMT>
 static hipError_t launch_fwd_v8_t(const FwdParams& p0, hipStream_t s) {
   FwdParams p = p0;
   p.n_qblocks = (p.Nq + 8 * kRowsPerWave - 1) / (8 * kRowsPerWave);
@@ -31,7 +31,8 @@ static hipError_t launch_fwd_v8_t(const FwdParams& p0, hipStream_t s) {
 
 template <typename T, int FMT>
 static hipError_t launch_fwd_v8_mask(const FwdParams& p, hipStream_t s) {
-  return p.mask != nullptr ? launch_fwd_v8_t<T, true, FMT>(p, s) : launch_fwd_v8_t<T, false, FMT>(p, s);
+  if (p.mask == nullptr) return launch_fwd_v8_t<T, kMaskNone, FMT>(p, s);
+  return p.mask_lds ? launch_fwd_v8_t<T, kMaskLds, FMT>(p, s) : launch_fwd_v8_t<T, kMaskGlobal, FMT>(p, s);
 }
 
 hipError_t launch_fwd_fp8v(const FwdParams& p, int dtype, int v_format, hipStream_t s) {

@@ -19,8 +19,8 @@
 //
 // Transposed products: the kernel computes S^T = K Q^T and O^T = V^T P^T.  In both
 // accumulators a lane owns one query COLUMN, so the per-query state (m, l, alpha) is one scalar
-// per lane and the score and output accumulators share it (Tylo "Online statistics": state and
-// values must agree on the reduced ownership).  The K rows fed to the first product are
+// per lane and the score and output accumulators share it (Tylo "Online statistics": a summary
+// serves only values distributed over the lanes the same way it is).  The K rows fed to the first product are
 // permuted (pi below) so that the fp32 score registers of a lane, packed pairwise to bf16/fp16,
 // ARE that lane's B operand of the second product: the accumulator-to-operand conversion needs
 // no lane exchange (the CDNA4 counterpart of Tylo's "Same-lane conversion").
@@ -49,6 +49,13 @@ constexpr int kMinBlockM = 4 * kRowsPerWave;   // smallest query block (four wav
 constexpr float kTau = 8.0f;
 constexpr float kTauPow = 256.0f;   // 2^TAU
 
+// Source of the byte mask, fixed per instantiation: a run-time choice inside the tile body would
+// split it into basic blocks, and the scheduler interleaves matrix and vector instructions only
+// inside one.
+constexpr int kMaskNone = 0;     // no byte mask
+constexpr int kMaskLds = 1;      // mask tiles staged into LDS with K and V (16-byte aligned rows)
+constexpr int kMaskGlobal = 2;   // mask bytes read from global memory (8 at a time when aligned)
+
 // LDS chunk swizzles (16-byte chunk index XOR, per key row).
 template <int SWZ>
 __device__ __forceinline__ int k_swz(int row) { return row & SWZ; }
@@ -61,7 +68,7 @@ template <int S> using stage_t = std::integral_constant<int, S>;
 // V8: 0 = V in T; 1 / 2 = V in E4M3 / E5M2 (one byte per element) and the second product on the
 // FP8 matrix cores (v_mfma_f32_32x32x64_f8f6f4, one 64-key tile per instruction) with P rounded
 // to E4M3.
-template <typename T, int D, int BN, bool MASK, bool SPLIT, int WAVES, int NSTAGES, int V8 = 0>
+template <typename T, int D, int BN, int MASK, bool SPLIT, int WAVES, int NSTAGES, int V8 = 0>
 __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void attn_fwd_kernel(FwdParams p) {
   using E = elem<T>;
   constexpr int kBlockM = WAVES * kRowsPerWave;
@@ -81,12 +88,12 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   // Mask tiles (MASK): the block's kBlockM query rows x BN key bytes, staged through LDS like K
   // and V.  Row r's 16-byte chunk c sits at position c ^ msw(r) of the row, so the 32 rows one
   // wave reads with a single instruction spread over the banks.
-  constexpr int MTILE = MASK ? kBlockM * BN : 0;
+  constexpr int MTILE = MASK == kMaskLds ? kBlockM * BN : 0;
   constexpr int M_CPR = BN / 16;                  // 16-byte chunks per mask row
   constexpr int M_RPI = 64 / M_CPR;               // mask rows per wave-instruction
   constexpr int M_RPL = 256 / BN;                 // mask rows per 256-byte bank line
-  constexpr int MPW = MASK ? MTILE / (1024 * WAVES) : 0;   // mask wave-instructions per wave per tile
-  static_assert(!MASK || MTILE % (1024 * WAVES) == 0, "whole mask wave-instructions per wave");
+  constexpr int MPW = MTILE / (1024 * WAVES);      // mask wave-instructions per wave per tile
+  static_assert(MTILE % (1024 * WAVES) == 0, "whole mask wave-instructions per wave");
   static_assert((WAVES * M_RPI / M_RPL) % M_CPR == 0, "mask swizzle independent of the instruction");
   static_assert(WAVES == 4 || WAVES == 8, "four or eight waves per workgroup");
   static_assert(TILE % 1024 == 0, "tile must be a whole number of 1 KiB wave loads");
@@ -191,7 +198,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   constexpr int kWaitAllButOneTileM = (kTileLoadsM & 15) | ((kTileLoadsM >> 4) << 14) | (7 << 4) | (15 << 8);
   // mask staging: lane offsets (row in the offset register, which the buffer bound checks: rows
   // at or past Nq, and bytes past the end of the mask, read as 0)
-  const bool use_lds_mask = MASK && p.mask_lds;
+  constexpr bool use_lds_mask = MASK == kMaskLds;
   auto msw = [](int r) { return (r / M_RPL) % M_CPR; };
   const int mrow0 = wave * M_RPI + lane / M_CPR;
   const uint32_t mo0 = (uint32_t)mrow0 * (uint32_t)p.Nkv + 16u * (uint32_t)((lane % M_CPR) ^ msw(mrow0));
@@ -250,16 +257,14 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv8, (__attribute__((address_space(3))) void*)(vdst + jj * WAVES * 1024), 16, vo8, 0, 0, 0);
       }
     }
-    if constexpr (MASK) {
-      if (use_lds_mask) {
-        uint8_t* mdst = lds + M_OFS + stage * MTILE + wave_lds;
-        const int64_t mbase = (int64_t)q_block0 * p.Nkv + k0;
-        const uint32_t mbytes = (uint32_t)((int64_t)p.Nq * p.Nkv - mbase);   // to the end of the mask
-        __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc((void*)(p.mask + mbase), 0, mbytes, 0x00020000);
+    if constexpr (use_lds_mask) {
+      uint8_t* mdst = lds + M_OFS + stage * MTILE + wave_lds;
+      const int64_t mbase = (int64_t)q_block0 * p.Nkv + k0;
+      const uint32_t mbytes = (uint32_t)((int64_t)p.Nq * p.Nkv - mbase);   // to the end of the mask
+      __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc((void*)(p.mask + mbase), 0, mbytes, 0x00020000);
 #pragma unroll
-        for (int i = 0; i < MPW; ++i)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (__attribute__((address_space(3))) void*)(mdst + i * WAVES * 1024), 16, mo0 + i * m_step, 0, 0, 0);
-      }
+      for (int i = 0; i < MPW; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (__attribute__((address_space(3))) void*)(mdst + i * WAVES * 1024), 16, mo0 + i * m_step, 0, 0, 0);
     }
   };
 
@@ -305,8 +310,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
       kaddr[ks] = lds + K_OFS + krow * RB + 16 * ((2 * ks + (lane >> 5)) ^ ksw);
   }
   // mask bytes of this lane's query row: chunk c (keys 16c .. 16c+15 of the tile), half kl
-  const uint8_t* maddr[MASK ? M_CPR : 1];
-  if constexpr (MASK) {
+  const uint8_t* maddr[use_lds_mask ? M_CPR : 1];
+  if constexpr (use_lds_mask) {
     const int rl = wave * kRowsPerWave + (lane & 31);
 #pragma unroll
     for (int c = 0; c < M_CPR; ++c) maddr[c] = lds + M_OFS + rl * BN + 16 * (c ^ msw(rl)) + kl;
@@ -355,8 +360,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
     // barrier's own fence does not wait for; with three stages the loads of tile t+1, issued
     // after it, may stay in flight); every wave done with tile t-1, whose stage is refilled next
     if (NSTAGE == 3 && t + 1 < ntiles) {
-      if (use_lds_mask) __builtin_amdgcn_s_waitcnt(kWaitAllButOneTileM);
-      else __builtin_amdgcn_s_waitcnt(kWaitAllButOneTile);
+      __builtin_amdgcn_s_waitcnt(use_lds_mask ? kWaitAllButOneTileM : kWaitAllButOneTile);
     } else {
       __builtin_amdgcn_s_waitcnt(0);
     }
@@ -401,43 +405,57 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
         for (int dt = 0; dt < DT; ++dt) oacc[dt] = E::mfma32(va[k2][dt], pb[k2], oacc[dt]);
     };
     // Masks (select to -inf).  Register r of block mt holds key
-    // k0 + 32*mt + 16*(r/8) + 8*(lane/32) + r%8 for query qi.
+    // k0 + 32*mt + 16*(r/8) + 8*(lane/32) + r%8 for query qi.  Returns whether any of the lane's
+    // 16 keys stays visible: the OR of the select conditions, which stay lane masks in scalar
+    // registers, so it costs scalar instructions only.
     auto mask_block = [&](int mt, f32x16& sa, auto masked_c) {
-      if constexpr (decltype(masked_c)::value) {
+      constexpr bool IDX = decltype(masked_c)::value;
+      if constexpr (!IDX && MASK == kMaskNone) {
+        return true;
+      } else {
+        bool vis[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * mt + 16 * (r >> 3) + kl + (r & 7);
-          const bool vis = (key < kend) && (!p.causal || key <= qi);
-          sa[r] = vis ? sa[r] : kNegInf;
+          vis[r] = IDX ? (key < kend) & (!p.causal | (key <= qi)) : true;
         }
-      }
-      if constexpr (MASK) {
-        const int qm = qi < p.Nq ? qi : p.Nq - 1;
-        const uint8_t* mrow = p.mask + (int64_t)qm * p.Nkv;
+        if constexpr (MASK != kMaskNone) {
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int key0 = k0 + 32 * mt + 16 * hf + kl;   // 8 consecutive keys
-          uint32_t lo = 0, hi = 0;
-          if (use_lds_mask) {
-            const u32x2 w = *reinterpret_cast<const u32x2*>(maddr[2 * mt + hf] + S * MTILE);
-            lo = w[0]; hi = w[1];
-          } else if (p.mask_vec && key0 + 8 <= p.Nkv) {
-            u32x2 w = *reinterpret_cast<const u32x2*>(mrow + key0);
-            lo = w[0]; hi = w[1];
-          } else {
+          for (int hf = 0; hf < 2; ++hf) {
+            const int key0 = k0 + 32 * mt + 16 * hf + kl;   // 8 consecutive keys
+            uint32_t lo = 0, hi = 0;
+            if constexpr (MASK == kMaskLds) {
+              const u32x2 w = *reinterpret_cast<const u32x2*>(maddr[2 * mt + hf] + S * MTILE);
+              lo = w[0]; hi = w[1];
+            } else {
+              const int qm = qi < p.Nq ? qi : p.Nq - 1;
+              const uint8_t* mrow = p.mask + (int64_t)qm * p.Nkv;
+              if (p.mask_vec && key0 + 8 <= p.Nkv) {
+                u32x2 w = *reinterpret_cast<const u32x2*>(mrow + key0);
+                lo = w[0]; hi = w[1];
+              } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                  const int key = key0 + j;
+                  uint32_t byte = key < p.Nkv ? mrow[key] : 0u;
+                  if (j < 4) lo |= byte << (8 * j); else hi |= byte << (8 * (j - 4));
+                }
+              }
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-              const int key = key0 + j;
-              uint32_t byte = key < p.Nkv ? mrow[key] : 0u;
-              if (j < 4) lo |= byte << (8 * j); else hi |= byte << (8 * (j - 4));
+              const uint32_t byte = (j < 4 ? (lo >> (8 * j)) : (hi >> (8 * (j - 4)))) & 0xFFu;
+              vis[8 * hf + j] = vis[8 * hf + j] & (byte != 0u);
             }
           }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const uint32_t byte = (j < 4 ? (lo >> (8 * j)) : (hi >> (8 * (j - 4)))) & 0xFFu;
-            sa[8 * hf + j] = byte ? sa[8 * hf + j] : kNegInf;
-          }
         }
+        bool any = false;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sa[r] = vis[r] ? sa[r] : kNegInf;
+          any = any | vis[r];
+        }
+        return any;
       }
     };
     // Weights of one 32-key block against reference mu, packed in place as the two B operands
@@ -466,29 +484,24 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
     // Softmax of one block, in two parts: start() masks and computes the weights against the
     // current reference; finish() is the lazy-rescale test, which the caller places after the
     // weights.  Only when some weight of the wave could exceed 2^TAU is the reference raised to
-    // the block maximum, the state rescaled and the block redone (rare, wave-uniform):
-    //   exact test (tiles with masked keys): block maximum > m + TAU;
-    //   sum test (every key visible): the lane's weight sum > 2^TAU, or no reference yet.  Every
-    //   weight is at most the sum, so a pass keeps every weight <= 2^TAU; and once a visible key
-    //   has set the reference (so l >= 1), weights that underflow to 0 are negligible.
-    struct BlockSm { float mx, ps; };
+    // the block maximum, the state rescaled and the block redone (rare, wave-uniform).  The test
+    // needs no block maximum: a lane's weight sum above 2^TAU (every weight is at most the sum,
+    // so a pass keeps each weight <= 2^TAU), or no reference yet while some key of the block is
+    // visible (a row with nothing visible so far keeps no reference and never raises it).  Once
+    // a visible key has set the reference (so l >= 1), weights that underflow to 0 are
+    // negligible.
+    struct BlockSm { float ps; bool any; };
     auto sm_start = [&](int mt, f32x16& sa, u32x4 (&pb)[2], auto masked_c) {
-      constexpr bool exact = decltype(masked_c)::value || MASK;
-      mask_block(mt, sa, masked_c);
-      BlockSm st{kNegInf, 0.f};
-      if constexpr (exact) st.mx = block_max(sa);
+      BlockSm st;
+      st.any = mask_block(mt, sa, masked_c);
       st.ps = weights(sa, (m_run == kNegInf) ? 0.f : m_run, pb);
       return st;
     };
-    auto sm_finish = [&](BlockSm st, const f32x16& sa, u32x4 (&pb)[2], auto masked_c) {
-      constexpr bool exact = decltype(masked_c)::value || MASK;
+    auto sm_finish = [&](BlockSm st, const f32x16& sa, u32x4 (&pb)[2], auto) {
       ATTN_PIN(st.ps);
-      bool raise;
-      if constexpr (exact) raise = __builtin_amdgcn_ballot_w64(st.mx > m_run + kTau) != 0;
-      else raise = __builtin_amdgcn_ballot_w64(st.ps > kTauPow || m_run == kNegInf) != 0;
+      const bool raise = __builtin_amdgcn_ballot_w64((st.ps > kTauPow) | ((m_run == kNegInf) & st.any)) != 0;
       if (raise) {
-        if constexpr (!exact) st.mx = block_max(sa);
-        const float m_new = fmaxf(m_run, st.mx);
+        const float m_new = fmaxf(m_run, block_max(sa));
         const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);   // 0 from empty
         l_run *= alpha;
 #pragma unroll
@@ -557,8 +570,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
       }
     };
     // ---- V8: both 32-key blocks of the tile are turned into weights first (the FP8 product
-    // consumes all 64 keys at once), so the lazy-rescale test is taken per tile: exact test on
-    // the larger block maximum, or the lane's weight sum over the tile.  Weights <= 2^TAU = 256
+    // consumes all 64 keys at once), so the lazy-rescale test is taken per tile, on the lane's
+    // weight sum over the tile (and on no reference yet while a key is visible).  Weights <= 2^TAU = 256
     // lie inside E4M3's range (448), so the round-to-nearest-even conversion never saturates.
     auto weights8 = [&](const f32x16& sa, float mu, i32x8& pb8, int mt) {
       float ps = 0.f;
@@ -577,10 +590,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
       return ps;
     };
     auto sm_start8 = [&](int mt, f32x16& sa, i32x8& pb8, auto masked_c) {
-      constexpr bool exact = decltype(masked_c)::value || MASK;
-      mask_block(mt, sa, masked_c);
-      BlockSm st{kNegInf, 0.f};
-      if constexpr (exact) st.mx = block_max(sa);
+      BlockSm st;
+      st.any = mask_block(mt, sa, masked_c);
       st.ps = weights8(sa, (m_run == kNegInf) ? 0.f : m_run, pb8, mt);
       return st;
     };
@@ -596,7 +607,6 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
       return va;
     };
     auto tile_body8 = [&](auto masked_c) {
-      constexpr bool exact = decltype(masked_c)::value || MASK;
       u32x4 kf[KSTEPS];
       read_k(0, kf);
       f32x16 s0 = qk(kf);
@@ -613,12 +623,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
       BlockSm st1 = sm_start8(1, s1, pb8, masked_c);
       ATTN_PIN(st0.ps);
       ATTN_PIN(st1.ps);
-      bool raise;
-      if constexpr (exact) raise = __builtin_amdgcn_ballot_w64(fmaxf(st0.mx, st1.mx) > m_run + kTau) != 0;
-      else raise = __builtin_amdgcn_ballot_w64(st0.ps + st1.ps > kTauPow || m_run == kNegInf) != 0;
+      const bool raise =
+          __builtin_amdgcn_ballot_w64((st0.ps + st1.ps > kTauPow) | ((m_run == kNegInf) & (st0.any | st1.any))) != 0;
       if (raise) {
-        const float mx = exact ? fmaxf(st0.mx, st1.mx) : fmaxf(block_max(s0), block_max(s1));
-        const float m_new = fmaxf(m_run, mx);
+        const float m_new = fmaxf(m_run, fmaxf(block_max(s0), block_max(s1)));
         const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);   // 0 from empty
         l_run *= alpha;
 #pragma unroll
@@ -704,7 +712,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
 // waves, two or more workgroups per CU.
 template <int D> constexpr int fwd_waves() { return D == 128 ? 8 : 4; }
 
-template <typename T, int D, int BN, bool MASK, bool SPLIT, int WAVES>
+template <typename T, int D, int BN, int MASK, bool SPLIT, int WAVES>
 inline hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t s) {
   constexpr int NSTAGES = WAVES == 8 ? 3 : 2;
   FwdParams p = p0;
@@ -717,9 +725,15 @@ inline hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t s) {
 template <typename T, int D, int BN>
 inline hipError_t launch_fwd_mask(const FwdParams& p, bool split, hipStream_t s) {
   constexpr int W = fwd_waves<D>();
-  const bool mask = p.mask != nullptr;
-  if (split) return mask ? launch_fwd_t<T, D, BN, true, true, W>(p, s) : launch_fwd_t<T, D, BN, false, true, W>(p, s);
-  return mask ? launch_fwd_t<T, D, BN, true, false, W>(p, s) : launch_fwd_t<T, D, BN, false, false, W>(p, s);
+  const int mask = p.mask == nullptr ? kMaskNone : (p.mask_lds ? kMaskLds : kMaskGlobal);
+  if (split) {
+    if (mask == kMaskLds) return launch_fwd_t<T, D, BN, kMaskLds, true, W>(p, s);
+    if (mask == kMaskGlobal) return launch_fwd_t<T, D, BN, kMaskGlobal, true, W>(p, s);
+    return launch_fwd_t<T, D, BN, kMaskNone, true, W>(p, s);
+  }
+  if (mask == kMaskLds) return launch_fwd_t<T, D, BN, kMaskLds, false, W>(p, s);
+  if (mask == kMaskGlobal) return launch_fwd_t<T, D, BN, kMaskGlobal, false, W>(p, s);
+  return launch_fwd_t<T, D, BN, kMaskNone, false, W>(p, s);
 }
 
 }  // namespace attn
