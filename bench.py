@@ -380,6 +380,14 @@ def main():
         # ---- the prefill with E4M3 V and an FP8 second product (right after the bf16 prefill,
         #      in the same state of the GPU) ----------------------------------------------------
         extra["fp8v_prefill"] = fp8v_figures(sa, dev, steps=args.steps, warmup=args.warmup, bf16_ms=t.get("prefill"))
+        # ---- the same tensors without the causal mask (context): per-FLOP rate of causal vs full
+        out_full = torch.empty_like(q)
+        _, mfull = timed_events([lambda: sa.attn_fwd(q, k, v, out_full, None, causal=False)], 10, 3)
+        fl_full = 4.0 * sp["D"] * sp["N"] * sp["N"] * sp["B"] * sp["H"]
+        extra["prefill_noncausal"] = {"ms": mfull[0], "TFLOP/s": fl_full / (mfull[0] * 1e-3) / 1e12,
+                                      "causal_per_flop_rate_vs_full": (fl / t["prefill"]) / (fl_full / mfull[0])
+                                      if "prefill" in t else None}
+        del out_full
         # ---- decode sweep over P (context) -------------------------------------------------
         sweep = {}
         for P in sd["P_list"]:

@@ -1,12 +1,13 @@
 // attn_combine.hip -- LSE-weighted merge of a split-K workspace (Modular MAX
 // "fa4_splitk_combine": per-row-head formulas, base 2 throughout, and its performance
 // structure), written for wave64:
-//   * one wave per output row-head (four per workgroup when there are many row-heads, one when
-//     there are few, so that a small merge spreads over more compute units); the row's depth is
-//     split into 16-byte lane slices, and 64 / (depth/4) partitions are folded side by side by
-//     separate lane groups;
-//   * the LSE reduction (max, log-sum-exp, per-partition scale) is computed once into lane
-//     registers: lane t holds partitions t, t+64, ...;
+//   * one wave per output row-head (four per workgroup when there are many row-heads), or, when
+//     there are few row-heads, the depth of each split over up to eight waves in workgroups of
+//     one, so that a small merge reaches ~1024 waves on the 256 compute units; a wave's depth
+//     slice is split into 16-byte lane slices, and 64 / (slice/4) partitions are folded side by
+//     side by separate lane groups;
+//   * each row-head's maximum, log-sum-exp and per-partition scales are reduced a single time,
+//     into lane registers: lane t holds partitions t, t+64, ...;
 //   * each partition's scale reaches its lane group by a cross-lane read (ds_bpermute) when
 //     P <= 64, or from a 256-entry LDS table beyond;
 //   * loads run ahead of the arithmetic: the first chunk of slices (16 per lane group) is issued
@@ -49,10 +50,11 @@ __device__ __forceinline__ f32x4 ld_stream(const float* a) {
 constexpr int kCombineChunk = 16;   // slices per lane group per chunk of loads
 
 // RUNG: the instantiation serves 1 <= P <= RUNG (RUNG = 4, 8, 16, 32 or 64), or any P up to
-// ATTN_P_MAX_DEV when RUNG = 0.  WAVES row-heads (one per wave) per workgroup.
-template <int RUNG, int DEPTH, typename TO, int WAVES>
+// ATTN_P_MAX_DEV when RUNG = 0.  DW: elements of the row-head's depth one wave merges (the
+// depth, or a power-of-two part of it).  WAVES waves per workgroup.
+template <int RUNG, int DW, typename TO, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void attn_combine_kernel(CombineParams p) {
-  constexpr int LPP = DEPTH / 4;              // lanes per partition slice (16 bytes each)
+  constexpr int LPP = DW / 4;                 // lanes per partition slice (16 bytes each)
   constexpr int G = 64 / LPP;                 // partitions folded side by side
   constexpr int NL = RUNG ? (RUNG + 63) / 64 : ATTN_P_MAX_DEV / 64;   // LSE registers per lane
   constexpr int NS = RUNG ? (RUNG + G - 1) / G : 0;                  // slices per lane group
@@ -64,14 +66,19 @@ __global__ __launch_bounds__(64 * WAVES) void attn_combine_kernel(CombineParams 
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t RH = p.RH;
+  const int depth = p.depth;
+  const int nsplit = depth / DW;              // waves per row-head
   // a wave past the last row-head computes on row-head RH-1 and stores nothing
-  const int64_t rh_w = (int64_t)blockIdx.x * WAVES + wave;
+  const int64_t w_all = (int64_t)blockIdx.x * WAVES + wave;
+  const int64_t rh_w = w_all / nsplit;
+  const int ds = (int)(w_all - rh_w * nsplit);   // this wave's depth slice
   const bool live = rh_w < RH;
   const int64_t rh = live ? rh_w : RH - 1;
 
   const int g = lane / LPP, dl = lane % LPP;
-  const int64_t pstride = RH * DEPTH;
-  const float* src = p.o_partial + rh * DEPTH + dl * 4;
+  const int64_t pstride = RH * depth;
+  const int64_t col = rh * depth + ds * DW + dl * 4;   // first of this lane's four elements
+  const float* src = p.o_partial + col;
   // slice i of chunk c of this lane group holds partition (c * CHS + i) * G + g
   auto load_chunk = [&](int c, f32x4 (&buf)[CHS]) {
 #pragma unroll
@@ -144,49 +151,57 @@ __global__ __launch_bounds__(64 * WAVES) void attn_combine_kernel(CombineParams 
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = across_groups_sum<LPP>(acc[j]);
-  if (live && g == 0) out_store<TO>::put4(p.out, rh * DEPTH + dl * 4, acc);
-  if (live && lane == 0 && p.lse_out) p.lse_out[rh] = empty ? kNegInf : Gl * kLn2;
+  if (live && g == 0) out_store<TO>::put4(p.out, col, acc);
+  if (live && ds == 0 && lane == 0 && p.lse_out) p.lse_out[rh] = empty ? kNegInf : Gl * kLn2;
 }
 
-// Row-heads per workgroup: four when there are enough row-heads to give every compute unit
-// several workgroups, else one (a decode-sized merge then reaches four times as many units).
-constexpr int64_t kCombineManyRH = 4 * 1024;
+// Waves per workgroup: four when the launch has enough waves to give every compute unit several
+// workgroups, else one (a decode-sized merge then spreads over more compute units).
+constexpr int64_t kCombineManyWaves = 4 * 1024;
+// Few row-heads: split each row-head's depth until the launch has this many waves.
+constexpr int64_t kCombineTargetWaves = 1024;
 
-template <int RUNG, int DEPTH, typename TO>
+template <int RUNG, int DW, typename TO>
 static void launch_combine_w(const CombineParams& p, hipStream_t s) {
-  if (p.RH >= kCombineManyRH)
-    hipLaunchKernelGGL((attn_combine_kernel<RUNG, DEPTH, TO, 4>), dim3((unsigned)((p.RH + 3) / 4)), dim3(256), 0, s, p);
+  const int64_t waves = p.RH * (p.depth / DW);
+  if (waves >= kCombineManyWaves)
+    hipLaunchKernelGGL((attn_combine_kernel<RUNG, DW, TO, 4>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((attn_combine_kernel<RUNG, DEPTH, TO, 1>), dim3((unsigned)p.RH), dim3(64), 0, s, p);
+    hipLaunchKernelGGL((attn_combine_kernel<RUNG, DW, TO, 1>), dim3((unsigned)waves), dim3(64), 0, s, p);
 }
 
-template <int RUNG, int DEPTH>
-static hipError_t launch_combine_t(const CombineParams& p, int out_dtype, hipStream_t s) {
-  if (out_dtype == 2) launch_combine_w<RUNG, DEPTH, float>(p, s);
-  else if (out_dtype == 0) launch_combine_w<RUNG, DEPTH, bf16_t>(p, s);
-  else launch_combine_w<RUNG, DEPTH, f16_t>(p, s);
+template <int RUNG, typename TO>
+static hipError_t launch_combine_dw(const CombineParams& p, hipStream_t s) {
+  int nsplit = 1;   // waves per row-head: a power of two, slices of at least 16 elements
+  while (nsplit < 8 && p.depth / (2 * nsplit) >= 16 && p.RH * nsplit < kCombineTargetWaves) nsplit *= 2;
+  switch (p.depth / nsplit) {
+    case 16: launch_combine_w<RUNG, 16, TO>(p, s); break;
+    case 32: launch_combine_w<RUNG, 32, TO>(p, s); break;
+    case 64: launch_combine_w<RUNG, 64, TO>(p, s); break;
+    case 128: launch_combine_w<RUNG, 128, TO>(p, s); break;
+    case 256: launch_combine_w<RUNG, 256, TO>(p, s); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
-template <int DEPTH>
-static hipError_t launch_combine_depth(const CombineParams& p, int out_dtype, hipStream_t s) {
-  if (p.P <= 4) return launch_combine_t<4, DEPTH>(p, out_dtype, s);
-  if (p.P <= 8) return launch_combine_t<8, DEPTH>(p, out_dtype, s);
-  if (p.P <= 16) return launch_combine_t<16, DEPTH>(p, out_dtype, s);
-  if (p.P <= 32) return launch_combine_t<32, DEPTH>(p, out_dtype, s);
-  if (p.P <= 64) return launch_combine_t<64, DEPTH>(p, out_dtype, s);
-  return launch_combine_t<0, DEPTH>(p, out_dtype, s);
+template <int RUNG>
+static hipError_t launch_combine_t(const CombineParams& p, int out_dtype, hipStream_t s) {
+  if (out_dtype == 2) return launch_combine_dw<RUNG, float>(p, s);
+  if (out_dtype == 0) return launch_combine_dw<RUNG, bf16_t>(p, s);
+  return launch_combine_dw<RUNG, f16_t>(p, s);
 }
 
-hipError_t launch_combine(const CombineParams& p, int depth, int out_dtype, hipStream_t s) {
-  switch (depth) {
-    case 16: return launch_combine_depth<16>(p, out_dtype, s);
-    case 32: return launch_combine_depth<32>(p, out_dtype, s);
-    case 64: return launch_combine_depth<64>(p, out_dtype, s);
-    case 128: return launch_combine_depth<128>(p, out_dtype, s);
-    case 256: return launch_combine_depth<256>(p, out_dtype, s);
-  }
-  return hipErrorInvalidValue;
+hipError_t launch_combine(const CombineParams& p0, int depth, int out_dtype, hipStream_t s) {
+  if (depth != 16 && depth != 32 && depth != 64 && depth != 128 && depth != 256) return hipErrorInvalidValue;
+  CombineParams p = p0;
+  p.depth = depth;
+  if (p.P <= 4) return launch_combine_t<4>(p, out_dtype, s);
+  if (p.P <= 8) return launch_combine_t<8>(p, out_dtype, s);
+  if (p.P <= 16) return launch_combine_t<16>(p, out_dtype, s);
+  if (p.P <= 32) return launch_combine_t<32>(p, out_dtype, s);
+  if (p.P <= 64) return launch_combine_t<64>(p, out_dtype, s);
+  return launch_combine_t<0>(p, out_dtype, s);
 }
 
 }  // namespace attn

@@ -59,6 +59,7 @@ struct CombineParams {
   float* lse_out;       // natural log, nullable
   int P;
   int RH;               // rows * heads
+  int depth;            // elements per row-head (set by launch_combine)
 };
 
 // Standalone row softmax (attn_softmax_rows).
