@@ -382,7 +382,7 @@ def main():
         extra["fp8v_prefill"] = fp8v_figures(sa, dev, steps=args.steps, warmup=args.warmup, bf16_ms=t.get("prefill"))
         # ---- the same tensors without the causal mask (context): per-FLOP rate of causal vs full
         out_full = torch.empty_like(q)
-        _, mfull = timed_events([lambda: sa.attn_fwd(q, k, v, out_full, None, causal=False)], 10, 3)
+        _, mfull = timed_events([lambda: sa.attn_fwd(q, k, v, out_full, None, causal=False)], args.steps, args.warmup)
         fl_full = 4.0 * sp["D"] * sp["N"] * sp["N"] * sp["B"] * sp["H"]
         extra["prefill_noncausal"] = {"ms": mfull[0], "TFLOP/s": fl_full / (mfull[0] * 1e-3) / 1e12,
                                       "causal_per_flop_rate_vs_full": (fl / t["prefill"]) / (fl_full / mfull[0])
