@@ -217,12 +217,22 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecodeParams p) {
       if (pp < p.P) sc_tab[pp] = (empty || lsv[j] == kNegInf) ? 0.f : fast_exp2(lsv[j] - Gl);
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");   // the table is complete before it is read
-    // weighted sum: lane covers d = lane + 64 i
+    // weighted sum: lane covers d = lane + 64 i; eight partitions' entries are loaded before any
+    // of them is folded, so the merge waits for ceil(P / 8) round trips to memory, not P
+    constexpr int kBatch = 8;
     for (int d = lane; d < D; d += 64) {
       float acc = 0.f;
-      for (int pp = 0; pp < p.P; ++pp) {
-        const float sp = sc_tab[pp];
-        if (sp != 0.f) acc = fmaf(sp, get_ws(p.o_partial + ((int64_t)pp * RH + rh) * D + d), acc);   // empty adds nothing
+      const float* col = p.o_partial + rh * D + d;
+      for (int pp0 = 0; pp0 < p.P; pp0 += kBatch) {
+        float x[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+          x[j] = pp0 + j < p.P ? get_ws(col + (int64_t)(pp0 + j) * RH * D) : 0.f;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const float sp = pp0 + j < p.P ? sc_tab[pp0 + j] : 0.f;
+          acc = sp != 0.f ? fmaf(sp, x[j], acc) : acc;   // an empty partition adds nothing
+        }
       }
       ((uint16_t*)p.out)[rh * D + d] = (uint16_t)(E::pack2(acc, 0.f) & 0xFFFFu);
     }
