@@ -21,12 +21,8 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int BN, bool split, 
 }
 
 template <typename T, int MASK, int FMT>
-static hipError_t launch_fwd_v8_t(const FwdParams& p0, hipStream_t s) {
-  FwdParams p = p0;
-  p.n_qblocks = (p.Nq + 8 * kRowsPerWave - 1) / (8 * kRowsPerWave);
-  dim3 grid((unsigned)((int64_t)p.n_qblocks * p.H * p.B));
-  hipLaunchKernelGGL((attn_fwd_kernel<T, 128, 64, MASK, false, 8, 3, FMT>), grid, dim3(512), 0, s, p);
-  return hipGetLastError();
+static hipError_t launch_fwd_v8_t(const FwdParams& p, hipStream_t s) {
+  return launch_fwd_t<T, 128, 64, MASK, false, 8, FMT>(p, s);
 }
 
 template <typename T, int FMT>

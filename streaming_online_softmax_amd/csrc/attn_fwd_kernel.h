@@ -68,7 +68,8 @@ template <int S> using stage_t = std::integral_constant<int, S>;
 // V8: 0 = V in T; 1 / 2 = V in E4M3 / E5M2 (one byte per element) and the second product on the
 // FP8 matrix cores (v_mfma_f32_32x32x64_f8f6f4, one 64-key tile per instruction) with P rounded
 // to E4M3.
-template <typename T, int D, int BN, int MASK, bool SPLIT, int WAVES, int NSTAGES, int V8 = 0>
+// PAIR (causal launches): a workgroup runs query blocks n-1-i and then i of one unit.
+template <typename T, int D, int BN, int MASK, bool SPLIT, int WAVES, int NSTAGES, int V8 = 0, bool PAIR = false>
 __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void attn_fwd_kernel(FwdParams p) {
   using E = elem<T>;
   constexpr int kBlockM = WAVES * kRowsPerWave;
@@ -133,26 +134,33 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   // ---- block coordinates.  Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8),
   //      so the linear order is remapped to give each XCD a contiguous run of blocks: the query
   //      blocks of one (head, batch) then run together on one XCD and share its L2 for K and V.
-  //      Causal blocks differ in length (query block i visits i+1 key blocks), so they are issued
-  //      longest first, and over PAIRS of heads: with one head at a time the long blocks of the
-  //      last heads would start late and finish after everything else.
+  //      Causal blocks differ in length (query block i visits i+1 key blocks).  With PAIR a
+  //      workgroup runs blocks n-1-i and i (n+1 key blocks in all), so every workgroup is equally
+  //      long and a CU is refilled as soon as its workgroup ends (workgroups that end at different
+  //      times leave CUs idle for microseconds between them); otherwise blocks are issued longest
+  //      first.  Both are issued over PAIRS of heads: with one head at a time the long blocks of
+  //      the last heads would start late and finish after everything else.
   int bid = blockIdx.x;
   if (gridDim.x % 8 == 0) bid = (bid % 8) * (gridDim.x / 8) + bid / 8;
   const int n_heads = p.H * p.B * p.P;                 // (head, batch, partition) units
+  const int per_unit = PAIR ? (p.n_qblocks + 1) / 2 : p.n_qblocks;   // workgroups per unit
   int hl, qb_idx;
   if (p.causal && n_heads % 2 == 0) {
     const int hh = bid & 1;
     bid >>= 1;
-    qb_idx = bid % p.n_qblocks;
-    hl = 2 * (bid / p.n_qblocks) + hh;
+    qb_idx = bid % per_unit;
+    hl = 2 * (bid / per_unit) + hh;
   } else {
-    qb_idx = bid % p.n_qblocks;
-    hl = bid / p.n_qblocks;
+    qb_idx = bid % per_unit;
+    hl = bid / per_unit;
   }
+  // the (first) block: causal ones longest first
+  const int qb_first = p.causal ? (p.n_qblocks - 1 - qb_idx) : qb_idx;
+
+  auto run_block = [&](const int qb) __attribute__((always_inline)) {
   const int h = hl % p.H;
   const int b = (hl / p.H) % p.B;
   const int part = hl / (p.H * p.B);
-  const int qb = p.causal ? (p.n_qblocks - 1 - qb_idx) : qb_idx;   // causal: longest first
 
   const int q_block0 = qb * kBlockM;
   const int q0 = q_block0 + wave * kRowsPerWave;   // first query row of this wave
@@ -704,7 +712,16 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
       if (lane < 32) p.lse_partial[prh] = l_all == 0.f ? kNegInf : m_run + log2f(l_all);
     }
   }
+  };
+  run_block(qb_first);
+  if constexpr (PAIR) {
+    if (2 * qb_idx != p.n_qblocks - 1) {   // the middle block of an odd count runs alone
+      __syncthreads();   // every wave done with the first block's stages before they are refilled
+      run_block(qb_idx);
+    }
+  }
 }
+
 
 // ---- host-side dispatch -------------------------------------------------------------------
 // D = 128 runs eight waves (256 query rows) per workgroup, one workgroup per CU: each K/V tile
@@ -712,13 +729,23 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
 // waves, two or more workgroups per CU.
 template <int D> constexpr int fwd_waves() { return D == 128 ? 8 : 4; }
 
-template <typename T, int D, int BN, int MASK, bool SPLIT, int WAVES>
+// Causal launches of the eight-wave kernel pair query blocks (PAIR); the pairing instantiation
+// is separate so that the others keep their single-block code.
+template <typename T, int D, int BN, int MASK, bool SPLIT, int WAVES, int V8 = 0>
 inline hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t s) {
   constexpr int NSTAGES = WAVES == 8 ? 3 : 2;
   FwdParams p = p0;
   p.n_qblocks = (p.Nq + WAVES * kRowsPerWave - 1) / (WAVES * kRowsPerWave);
-  dim3 grid((unsigned)((int64_t)p.n_qblocks * p.H * p.B * p.P));
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, MASK, SPLIT, WAVES, NSTAGES>), grid, dim3(64 * WAVES), 0, s, p);
+  const int64_t units = (int64_t)p.H * p.B * p.P;
+  if constexpr (WAVES == 8 && !SPLIT) {
+    if (p.causal && p.n_qblocks > 1) {
+      dim3 grid((unsigned)(units * ((p.n_qblocks + 1) / 2)));
+      hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, MASK, SPLIT, WAVES, NSTAGES, V8, true>), grid, dim3(64 * WAVES), 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  dim3 grid((unsigned)(units * p.n_qblocks));
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, BN, MASK, SPLIT, WAVES, NSTAGES, V8>), grid, dim3(64 * WAVES), 0, s, p);
   return hipGetLastError();
 }
 
