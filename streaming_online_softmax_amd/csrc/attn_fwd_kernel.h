@@ -157,7 +157,24 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   // the (first) block: causal ones longest first
   const int qb_first = p.causal ? (p.n_qblocks - 1 - qb_idx) : qb_idx;
 
-  auto run_block = [&](const int qb) __attribute__((always_inline)) {
+  // With PAIR, the second block's Q rows are loaded into qn at the end of the first block's tile
+  // loop: their latency then overlaps the first block's epilogue and the barrier between the
+  // blocks (where the waves whose rows left the causal diagonal first wait for the others).
+  u32x4 qn[PAIR ? KSTEPS : 1];
+  auto load_q = [&](int qb, u32x4* dst) __attribute__((always_inline)) {
+    const int h = hl % p.H, b = (hl / p.H) % p.B;
+    const int qi = qb * kBlockM + wave * kRowsPerWave + (lane & 31);
+    const bool ok = qi < p.Nq;
+    const uint16_t* qrow = (const uint16_t*)p.q + ((int64_t)b * p.Nq * p.H + h) * D + (int64_t)(ok ? qi : 0) * ((int64_t)p.H * D) + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      u32x4 v = ld16(qrow + 16 * ks);
+      dst[ks] = ok ? v : u32x4{0, 0, 0, 0};
+    }
+  };
+  // blk_c: 0 = a single block, 1 = the first block of a pair, 2 = the second
+  auto run_block = [&](const int qb, auto blk_c) __attribute__((always_inline)) {
+    constexpr int BLK = decltype(blk_c)::value;
   const int h = hl % p.H;
   const int b = (hl / p.H) % p.B;
   const int part = hl / (p.H * p.B);
@@ -278,7 +295,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
 
   // ---- Q^T as the B operand of S^T = K Q^T: lane holds Q[qi][16*ks + 8*(lane/32) .. +8]
   u32x4 qf[KSTEPS];
-  {
+  if constexpr (BLK == 2) {
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = qn[ks];
+  } else {
     const bool ok = qi < p.Nq;
     const uint16_t* qrow = qbase + (int64_t)(ok ? qi : 0) * row_stride + 8 * (lane >> 5);
 #pragma unroll
@@ -671,6 +691,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
       if (t + 2 < ntiles) do_tile(t + 2, stage_t<2>{});
   }
 
+  if constexpr (BLK == 1) load_q(qb_idx, qn);   // the pair's second block
+
   // ---- epilogue: finish the denominator over the lane pair, normalise, store
   const float l_all = xor32_sum(l_run);
   const float inv = l_all == 0.f ? 0.f : (V8 ? p.v_scale : 1.f) / l_all;   // V8: V's scale folded in
@@ -713,12 +735,16 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
     }
   }
   };
-  run_block(qb_first);
   if constexpr (PAIR) {
-    if (2 * qb_idx != p.n_qblocks - 1) {   // the middle block of an odd count runs alone
+    if (2 * qb_idx != p.n_qblocks - 1) {
+      run_block(qb_first, std::integral_constant<int, 1>{});
       __syncthreads();   // every wave done with the first block's stages before they are refilled
-      run_block(qb_idx);
+      run_block(qb_idx, std::integral_constant<int, 2>{});
+    } else {   // the middle block of an odd count runs alone
+      run_block(qb_first, std::integral_constant<int, 0>{});
     }
+  } else {
+    run_block(qb_first, std::integral_constant<int, 0>{});
   }
 }
 
