@@ -12,7 +12,8 @@ beside it, together with a decode sweep over P in {4, 8, 16, 37} (two launches, 
 work fused into one attn_fwd_splitk_fused launch) and a combine measured on a workspace too large
 for the caches, the standalone row softmax (three methods) on 32768 x 4096 and 4096 x 32768
 fp32 rows, the masked long-context prefill (B1 H16 N16384 D256, causal AND a Bernoulli(0.5)
-mask with 1/64 of the rows fully masked) beside the same shape without the mask, the prefill
+mask with 1/64 of the rows fully masked: the mask packed to bits, then the forward on the bits;
+the forward on the byte mask and the same shape without the mask beside it), the prefill
 with E4M3 V on the FP8 matrix cores (attn_fwd_fp8v), the decode-shape combine on cold workspaces
 (cycling through more than 1 GiB of them), 32- vs 64-key tiles on a single-head N2048 D64 shape,
 and the shader clock rocm-smi reports right after the timed region.  Every per-kernel time comes
@@ -74,10 +75,20 @@ def softmax_figures(sa, dev, steps=10, warmup=3):
     return res
 
 
+def mask_pack_bytes(N):
+    """Bytes a causal attn_mask_pack of an N x N mask moves: the mask bytes of the groups it
+    writes (64-key groups c with 64 c <= 32 g + 31 for 32-row groups g), and their words."""
+    ng, nkg = -(-N // 32), -(-N // 64)
+    groups = sum(min(nkg, (32 * g + 31) // 64 + 1) for g in range(ng))
+    return groups * (32 * 64 + 64 * 4)
+
+
 def masked_figures(sa, dev, steps=10, warmup=3):
-    """attn_fwd on the masked long-context workload, and on the same tensors without the mask.
-    TFLOP/s counts 4*D per causal pair (the work the kernel does); 'useful' counts only the pairs
-    the mask leaves visible."""
+    """The masked long-context workload, and the same tensors without the mask.  The masked step
+    is attn_mask_pack (the byte mask to packed bits, causal half) followed by the forward reading
+    the bits; the forward reading the byte mask directly is timed beside it.  TFLOP/s counts 4*D
+    per causal pair (the work the kernel does); 'useful' counts only the pairs the mask leaves
+    visible."""
     s = si.MASKED
     qc, kc, vc, mask, _ = si.masked_inputs()
     vis = 0
@@ -89,14 +100,25 @@ def masked_figures(sa, dev, steps=10, warmup=3):
     del qc, kc, vc, mask
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    bits = torch.empty(sa.mask_bits_words(s["N"], s["N"]), dtype=torch.int32, device=dev)
     fl = prefill_flops(s["B"], s["H"], s["N"], s["D"])
     useful = 4.0 * s["D"] * vis * s["B"] * s["H"]
-    _, m = timed_events([lambda: sa.attn_fwd(q, k, v, out, lse, causal=True, mask=md),
+
+    def packed_step():
+        sa.attn_mask_pack(md, bits, causal=True)
+        sa.attn_fwd(q, k, v, out, lse, causal=True, mask_bits=bits)
+    _, m = timed_events([packed_step,
+                         lambda: sa.attn_mask_pack(md, bits, causal=True),
+                         lambda: sa.attn_fwd(q, k, v, out, lse, causal=True, mask=md),
                          lambda: sa.attn_fwd(q, k, v, out, lse, causal=True)], steps, warmup)
-    return {"B": s["B"], "H": s["H"], "N": s["N"], "D": s["D"], "masked_ms": m[0],
+    return {"B": s["B"], "H": s["H"], "N": s["N"], "D": s["D"],
+            "step": "attn_mask_pack(causal) + attn_fwd(mask_bits)", "masked_ms": m[0],
             "masked_TFLOP/s": fl / (m[0] * 1e-3) / 1e12, "mfma_frac": fl / (m[0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "useful_TFLOP/s": useful / (m[0] * 1e-3) / 1e12, "visible_pair_frac": vis / (s["N"] * (s["N"] + 1) / 2),
-            "causal_only_ms": m[1], "causal_only_TFLOP/s": fl / (m[1] * 1e-3) / 1e12}
+            "pack_ms": m[1], "pack_GB/s": mask_pack_bytes(s["N"]) / (m[1] * 1e-3) / 1e9,
+            "byte_mask_ms": m[2], "byte_mask_TFLOP/s": fl / (m[2] * 1e-3) / 1e12,
+            "causal_only_ms": m[3], "causal_only_TFLOP/s": fl / (m[3] * 1e-3) / 1e12,
+            "masked_over_causal_only": m[0] / m[3]}
 
 
 def fp8v_figures(sa, dev, steps=10, warmup=3, bf16_ms=None):

@@ -26,6 +26,10 @@
  *                    matrix cores.
  *   attn_round       FP32 -> bf16 / fp16 / E4M3 with the conversion the kernels apply to the
  *                    probabilities and to the output (exposed so it can be checked bit by bit).
+ *   attn_mask_pack   a byte mask re-encoded as one bit per (query, key), in the order the
+ *                    attention kernels hold scores in their registers; attn_fwd_packed is
+ *                    attn_fwd reading that encoding (one 32-bit word per lane per 64 keys
+ *                    instead of 64 bytes), for masks used more than once or read by many heads.
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library allocates
@@ -61,7 +65,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 #define ATTN_P_MAX 256 /* largest split count: one partition per MI355X compute unit */
 #define ATTN_TICKET_STRIDE 32 /* uint32 slots per row-head in a fused-decode ticket array (128 B) */
 #define ATTN_NOALLOC_SCRATCH_BYTES (64u << 20) /* per-GPU workspace of attn_fwd_splitk_noalloc */
@@ -222,7 +226,8 @@ int attn_softmax_rows(const void* x, void* y, int64_t rows, int n, int dtype, in
  */
 int attn_round(const float* x, void* y, int64_t n, int dtype, void* stream);
 
-/* Extended forward call for tests and tuning: every attn_fwd argument plus the key-tile width. */
+/* Extended forward call for tests and tuning: every attn_fwd argument plus the key-tile width
+ * and the packed mask of attn_fwd_packed (at most one of mask and mask_bits). */
 struct attn_fwd_args {
   const void* q;
   const void* k;
@@ -234,6 +239,7 @@ struct attn_fwd_args {
   int causal;
   int dtype;
   int block_n;         /* key-tile width: 0 = library default, else 32 or 64 (32 only for D <= 64) */
+  const uint32_t* mask_bits; /* nullable; as attn_fwd_packed, packed with the same causal flag */
 };
 int attn_fwd_ex(const struct attn_fwd_args* a, void* stream);
 
@@ -260,6 +266,43 @@ int attn_fwd_ex(const struct attn_fwd_args* a, void* stream);
  */
 int attn_fwd_fp8v(const void* q, const void* k, const uint8_t* v, int v_format, float v_scale, void* out,
                   float* lse, int B, int H, int N, int D, int causal, const uint8_t* mask, int dtype, void* stream);
+
+/*
+ * Packed masks.  The mask semantics are attn_fwd's (a key is visible where the byte is nonzero:
+ * triton-cuda-lab workshop "A3. Tiled attention with online normalization", section "Masks that
+ * preserve the recurrence"); the encoding is this library's, chosen so that each lane of a
+ * 64-wide wavefront loads the visibility of exactly the scores it holds.  With Nq x Nkv bytes
+ * of mask, ATTN_MASK_BITS_WORDS(Nq, Nkv) uint32 words: for row group g (rows 32 g .. 32 g + 31),
+ * key group c (keys 64 c .. 64 c + 63) and lane l (0 .. 63), word (g * ceil(Nkv / 64) + c) * 64
+ * + l has bit b (0 .. 31) set iff row 32 g + l % 32 and key
+ *     64 c + 32 (b / 16) + 16 ((b % 16) / 8) + 8 (l / 32) + b % 8
+ * are inside the mask and its byte is nonzero.
+ */
+#define ATTN_MASK_BITS_WORDS(Nq, Nkv) \
+  ((((int64_t)(Nq) + 31) / 32) * (((int64_t)(Nkv) + 63) / 64) * 64)
+
+/*
+ * attn_mask_pack -- encode a byte mask as above.
+ *   mask    uint8 [Nq, Nkv] row-major, device, read only (any alignment).
+ *   Nq, Nkv >= 1.
+ *   causal  0: every word is written.  1 (requires Nq == Nkv): only the groups a causal forward
+ *           reads are written, those with 64 c <= 32 g + 31; the mask bytes above them are not
+ *           read and the other words are left as they were.  Bits packed with causal = 1 serve
+ *           causal forward calls only.
+ *   bits    ATTN_MASK_BITS_WORDS(Nq, Nkv) uint32, device, 4-byte aligned, written.
+ *   Errors: ATTN_E_NULL, ATTN_E_SHAPE (sizes, causal with Nq != Nkv), ATTN_E_ALIGN (bits),
+ *   ATTN_E_HIP.
+ */
+int attn_mask_pack(const uint8_t* mask, int Nq, int Nkv, int causal, uint32_t* bits, void* stream);
+
+/*
+ * attn_fwd_packed -- attn_fwd with the mask given as attn_mask_pack's bits (of the N x N mask,
+ *   packed with the same causal flag); mask_bits is required.  Results are bit for bit those of
+ *   attn_fwd with the byte mask.  Other arguments and errors: as attn_fwd; ATTN_E_NULL without
+ *   mask_bits, ATTN_E_ALIGN unless it is 4-byte aligned.
+ */
+int attn_fwd_packed(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int N,
+                    int D, int causal, const uint32_t* mask_bits, int dtype, void* stream);
 
 /* Message describing the calling thread's last non-OK return ("" if none). */
 const char* attn_last_error(void);

@@ -5,7 +5,10 @@ libattn.so (built from ``csrc/`` by ``build.py``).  torch supplies device memory
 If the library has not been built, the first call raises -- there is no fallback.
 
 Entry points (same names as the C ABI in include/attn.h):
-    attn_fwd(q, k, v, out, lse=None, causal=False, mask=None, block_n=0, stream=None)
+    attn_fwd(q, k, v, out, lse=None, causal=False, mask=None, block_n=0, stream=None, mask_bits=None)
+    attn_fwd_packed(q, k, v, out, lse=None, causal=False, mask_bits=..., stream=None)
+    attn_mask_pack(mask, bits, causal=False, stream=None)
+                    (mask uint8 [Nq, Nkv]; bits int32 of mask_bits_words(Nq, Nkv) elements)
     attn_fwd_splitk(q, k, v, P, o_partial, lse_partial, out=None, lse=None, causal=False,
                     mask=None, stream=None)
     attn_fwd_splitk_fused(q, k, v, P, o_partial, lse_partial, tickets, out, lse=None, causal=False,
@@ -20,7 +23,8 @@ Entry points (same names as the C ABI in include/attn.h):
 Tensors are torch tensors on the GPU, contiguous, laid out as the header states
 (q/out [B, Nq, H, D]; k/v [B, Nkv, H, D]; o_partial [P, B*Nq, H, D]; lse_partial [P, B*Nq, H];
 tickets int32 [B*Nq*H*TICKET_STRIDE], zero before the first call and left zero by every call).
-Allocating helpers fwd(), fwd_fp8v(), splitk(), splitk_fused() and combine() return fresh outputs.
+Allocating helpers fwd(), fwd_fp8v(), splitk(), splitk_fused(), combine() and pack_mask() return
+fresh outputs.
 """
 import ctypes
 import os
@@ -51,7 +55,8 @@ class FwdArgs(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("mask", ctypes.c_void_p),
                 ("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int), ("D", ctypes.c_int),
-                ("causal", ctypes.c_int), ("dtype", ctypes.c_int), ("block_n", ctypes.c_int)]
+                ("causal", ctypes.c_int), ("dtype", ctypes.c_int), ("block_n", ctypes.c_int),
+                ("mask_bits", ctypes.c_void_p)]
 
 
 _LIB = None
@@ -86,6 +91,10 @@ def _load():
     L.attn_round.restype = i32
     L.attn_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     L.attn_combine.restype = i32
+    L.attn_fwd_packed.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, vp]
+    L.attn_fwd_packed.restype = i32
+    L.attn_mask_pack.argtypes = [vp, i32, i32, i32, vp, vp]
+    L.attn_mask_pack.restype = i32
     L.attn_fwd_ex.argtypes = [ctypes.POINTER(FwdArgs), vp]
     L.attn_fwd_ex.restype = i32
     L.attn_last_error.restype = ctypes.c_char_p
@@ -137,11 +146,29 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def attn_fwd(q, k, v, out, lse=None, causal=False, mask=None, block_n=0, stream=None):
+def attn_fwd(q, k, v, out, lse=None, causal=False, mask=None, block_n=0, stream=None, mask_bits=None):
     B, N, H, D = q.shape
     a = FwdArgs(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(mask),
-                B, H, N, D, int(causal), _dtype_code(q), int(block_n))
+                B, H, N, D, int(causal), _dtype_code(q), int(block_n), _ptr(mask_bits))
     _check(lib().attn_fwd_ex(ctypes.byref(a), _stream(stream)))
+
+
+def attn_fwd_packed(q, k, v, out, lse=None, causal=False, mask_bits=None, stream=None):
+    B, N, H, D = q.shape
+    _check(lib().attn_fwd_packed(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, D, int(causal),
+                                 _ptr(mask_bits), _dtype_code(q), _stream(stream)))
+
+
+def mask_bits_words(Nq, Nkv):
+    """32-bit words of a packed Nq x Nkv mask (ATTN_MASK_BITS_WORDS)."""
+    return ((Nq + 31) // 32) * ((Nkv + 63) // 64) * 64
+
+
+def attn_mask_pack(mask, bits, causal=False, stream=None):
+    Nq, Nkv = mask.shape
+    if bits.numel() != mask_bits_words(Nq, Nkv) or bits.element_size() != 4:
+        raise AttnError(2, f"bits must hold {mask_bits_words(Nq, Nkv)} 32-bit words")
+    _check(lib().attn_mask_pack(_ptr(mask), Nq, Nkv, int(causal), _ptr(bits), _stream(stream)))
 
 
 def attn_fwd_splitk(q, k, v, P, o_partial, lse_partial, out=None, lse=None, causal=False, mask=None,
@@ -218,11 +245,19 @@ def attn_fwd_fp8v(q, k, v, v_scale, out, lse=None, causal=False, mask=None, v_fo
 
 
 # ---- allocating helpers -------------------------------------------------------------------
-def fwd(q, k, v, causal=False, mask=None, block_n=0, with_lse=True):
+def fwd(q, k, v, causal=False, mask=None, block_n=0, with_lse=True, mask_bits=None):
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if with_lse else None
-    attn_fwd(q, k, v, out, lse, causal=causal, mask=mask, block_n=block_n)
+    attn_fwd(q, k, v, out, lse, causal=causal, mask=mask, block_n=block_n, mask_bits=mask_bits)
     return out, lse
+
+
+def pack_mask(mask, causal=False):
+    """attn_mask_pack into a fresh int32 tensor (words of a causal packing above the diagonal
+    are left unset)."""
+    bits = torch.empty(mask_bits_words(*mask.shape), dtype=torch.int32, device=mask.device)
+    attn_mask_pack(mask, bits, causal=causal)
+    return bits
 
 
 def fwd_fp8v(q, k, v, v_scale=1.0, causal=False, mask=None, v_format=None):

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattn.so")
 SOURCES = ["api.cpp", "attn_fwd.hip", "attn_fwd_d256.hip", "attn_decode.hip", "attn_combine.hip", "softmax_rows.hip",
-           "convert.hip"]
+           "convert.hip", "mask_pack.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",

@@ -130,6 +130,8 @@ int fwd_impl(const attn_fwd_args* a, hipStream_t s) {
   if (!a->out) return fail(ATTN_E_NULL, "out must be a non-NULL device pointer");
   if (!aligned(a->out, 16)) return fail(ATTN_E_ALIGN, "out must be 16-byte aligned");
   if (a->lse && !aligned(a->lse, 4)) return fail(ATTN_E_ALIGN, "lse must be 4-byte aligned");
+  if (a->mask && a->mask_bits) return fail(ATTN_E_SHAPE, "give the mask as bytes or as packed bits, not both");
+  if (a->mask_bits && !aligned(a->mask_bits, 4)) return fail(ATTN_E_ALIGN, "mask_bits must be 4-byte aligned");
   int BN = a->block_n;
   if (BN == 0) BN = 64;
   if (BN != 32 && BN != 64) return fail(ATTN_E_UNSUPPORTED, "block_n=%d not supported (32 or 64)", a->block_n);
@@ -147,6 +149,8 @@ int fwd_impl(const attn_fwd_args* a, hipStream_t s) {
   p.n_qblocks = (int)nqb;
   p.mask_vec = a->mask && aligned(a->mask, 8) && (a->N % 8 == 0);
   p.mask_lds = a->mask && aligned(a->mask, 16) && (a->N % 16 == 0) && ((int64_t)a->N + 256) * a->N < (1LL << 32);
+  p.mask_bits = a->mask_bits;
+  p.n_kgroups = (a->N + 63) / 64;
   p.scale_log2 = scale_log2(a->D);
   return hip_status(attn::launch_fwd(p, a->dtype, a->D, BN, false, s), "attn_fwd launch");
 }
@@ -205,6 +209,27 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.mask = mask;
   a.B = B; a.H = H; a.N = N; a.D = D; a.causal = causal; a.dtype = dtype; a.block_n = 0;
   return fwd_impl(&a, (hipStream_t)stream);
+}
+
+int attn_fwd_packed(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int N,
+                    int D, int causal, const uint32_t* mask_bits, int dtype, void* stream) {
+  if (!mask_bits) return fail(ATTN_E_NULL, "mask_bits must be a non-NULL device pointer");
+  attn_fwd_args a{};
+  a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.mask_bits = mask_bits;
+  a.B = B; a.H = H; a.N = N; a.D = D; a.causal = causal; a.dtype = dtype; a.block_n = 0;
+  return fwd_impl(&a, (hipStream_t)stream);
+}
+
+int attn_mask_pack(const uint8_t* mask, int Nq, int Nkv, int causal, uint32_t* bits, void* stream) {
+  if (!mask || !bits) return fail(ATTN_E_NULL, "mask and bits must be non-NULL device pointers");
+  if (Nq < 1 || Nkv < 1) return fail(ATTN_E_SHAPE, "Nq and Nkv must be >= 1 (got %d, %d)", Nq, Nkv);
+  if (causal != 0 && causal != 1) return fail(ATTN_E_SHAPE, "causal must be 0 or 1 (got %d)", causal);
+  if (causal && Nq != Nkv) return fail(ATTN_E_SHAPE, "causal packing requires Nq == Nkv (got %d, %d)", Nq, Nkv);
+  if (!aligned(bits, 4)) return fail(ATTN_E_ALIGN, "bits must be 4-byte aligned");
+  if ((double)Nq * Nkv > 9.0e18) return fail(ATTN_E_SHAPE, "mask size overflows");
+  if ((((int64_t)Nq + 31) / 32) * ((((int64_t)Nkv + 63) / 64 + 3) / 4) > 0x7fffffffLL)
+    return fail(ATTN_E_SHAPE, "grid too large");
+  return hip_status(attn::launch_mask_pack(mask, Nq, Nkv, causal, bits, (hipStream_t)stream), "attn_mask_pack launch");
 }
 
 int attn_fwd_ex(const struct attn_fwd_args* a, void* stream) {

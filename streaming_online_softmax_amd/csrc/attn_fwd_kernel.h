@@ -55,6 +55,8 @@ constexpr float kTauPow = 256.0f;   // 2^TAU
 constexpr int kMaskNone = 0;     // no byte mask
 constexpr int kMaskLds = 1;      // mask tiles staged into LDS with K and V (16-byte aligned rows)
 constexpr int kMaskGlobal = 2;   // mask bytes read from global memory (8 at a time when aligned)
+constexpr int kMaskBits = 3;     // packed mask (attn_mask_pack): one word per lane per 64 keys,
+                                 // loaded a tile ahead into a register (unsplit launches)
 
 // LDS chunk swizzles (16-byte chunk index XOR, per key row).
 template <int SWZ>
@@ -63,6 +65,32 @@ template <int RPB, int BITS>
 __device__ __forceinline__ int v_swz(int row) { return BITS ? 4 * ((row / RPB) & BITS) : 0; }
 
 template <int S> using stage_t = std::integral_constant<int, S>;
+
+// s where bit b of w is set, else -inf: the bit sign-extended to a full mask (one bit-field
+// extract), then one bit-field select between s and -inf.
+__device__ __forceinline__ float keep_if_bit(uint32_t w, int b, float s) {
+  const uint32_t m = (uint32_t)((int32_t)(w << (31 - b)) >> 31);
+  return __uint_as_float((__float_as_uint(s) & m) | (0xff800000u & ~m));
+}
+
+// s where byte B of w is nonzero, else -inf: one compare of the byte against 0 (SDWA operand
+// select) into a lane mask, and one select.  Only the compare is written out (the compiler
+// extracts most bytes with a separate AND or shift first); the select stays compiler-generated
+// because s is usually a matrix-core result, whose read-after-write wait states the compiler
+// inserts for its own instructions but not for inline asm.
+template <int B>
+__device__ __forceinline__ float keep_if_byte(uint32_t w, float s) {
+  static_assert(B >= 0 && B < 4, "byte index");
+  uint64_t m;
+#define ATTN_BYTE_NZ(SEL) \
+  asm("v_cmp_ne_u32_sdwa %0, %1, %2 src0_sel:" SEL " src1_sel:DWORD" : "=s"(m) : "v"(w), "v"(0u))
+  if constexpr (B == 0) ATTN_BYTE_NZ("BYTE_0");
+  else if constexpr (B == 1) ATTN_BYTE_NZ("BYTE_1");
+  else if constexpr (B == 2) ATTN_BYTE_NZ("BYTE_2");
+  else ATTN_BYTE_NZ("BYTE_3");
+#undef ATTN_BYTE_NZ
+  return __builtin_amdgcn_inverse_ballot_w64(m) ? s : -__builtin_inff();
+}
 
 // WAVES waves of 32 query rows each; BN keys per tile.
 // V8: 0 = V in T; 1 / 2 = V in E4M3 / E5M2 (one byte per element) and the second product on the
@@ -102,6 +130,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   // chunk ^ (2 * ((row / 2) % 4)): the 8 rows x 2 chunks that one half-wave of a byte-transposing
   // read touches then cover the 64 banks exactly once.
   static_assert(!V8 || (D == 128 && BN == 64 && !SPLIT), "the FP8 second product is built for D = 128, 64-key tiles");
+  static_assert(MASK != kMaskBits || !SPLIT, "packed masks assume key tiles aligned to 64 keys");
   constexpr int RBV = V8 ? D : RB;      // bytes per V row in LDS
   constexpr int TILEV = BN * RBV;
   constexpr int NTV = TILEV / 1024;
@@ -190,6 +219,20 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   }
   if (p.causal) kend = min(kend, q_block0 + kBlockM);   // keys beyond the block's last row are future
   const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
+
+  // ---- packed mask: word ((q0 / 32) * n_kgroups + key group) * 64 + lane holds this lane's
+  //      scores of 64 keys, bit 16 mt + r for register r of 32-key block mt.  The word of tile
+  //      t + 1 is loaded while tile t runs (a 32-key tile takes its half of the word).
+  constexpr bool use_bits = MASK == kMaskBits;
+  const uint32_t* mbits_lane = use_bits ? p.mask_bits + (int64_t)(q0 >> 5) * p.n_kgroups * 64 + lane : nullptr;
+  auto load_bits = [&](int t) -> uint32_t {
+    const int kt = t * BN;
+    const uint32_t w = mbits_lane[(int64_t)(kt >> 6) * 64];
+    return BN == 32 ? (w >> (16 * ((kt >> 5) & 1))) : w;
+  };
+  uint32_t mbits_next = 0;
+  if constexpr (use_bits)
+    if (q0 < p.Nq && ntiles > 0) mbits_next = load_bits(0);
 
   const int64_t row_stride = (int64_t)p.H * D;            // elements between consecutive tokens
   const uint16_t* qbase = (const uint16_t*)p.q + ((int64_t)b * p.Nq * p.H + h) * D;
@@ -393,6 +436,13 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
       __builtin_amdgcn_s_waitcnt(0);
     }
     __syncthreads();
+    uint32_t mw = 0;   // packed mask word of this tile
+    if constexpr (use_bits) {
+      // issued before the next stage's loads, so that the count-based wait at the start of tile
+      // t + 1 (all but that stage's loads) covers it
+      mw = mbits_next;
+      if (t + 1 < ntiles && q0 < p.Nq && !(p.causal && k0 + BN > q0 + kRowsPerWave - 1)) mbits_next = load_bits(t + 1);
+    }
     if (t + NSTAGE - 1 < ntiles) issue_tile(t + NSTAGE - 1, (S + NSTAGE - 1) % NSTAGE);
 
     // wave-uniform decisions for this tile
@@ -436,10 +486,50 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
     // k0 + 32*mt + 16*(r/8) + 8*(lane/32) + r%8 for query qi.  Returns whether any of the lane's
     // 16 keys stays visible: the OR of the select conditions, which stay lane masks in scalar
     // registers, so it costs scalar instructions only.
+    // the byte-mask words of block mt, keys 16*hf .. +8 (lo: bytes 0-3, hi: 4-7)
+    auto mask_words = [&](int mt, int hf, uint32_t& lo, uint32_t& hi) {
+      const int key0 = k0 + 32 * mt + 16 * hf + kl;   // 8 consecutive keys
+      lo = 0; hi = 0;
+      if constexpr (MASK == kMaskLds) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(maddr[2 * mt + hf] + S * MTILE);
+        lo = w[0]; hi = w[1];
+      } else {
+        const int qm = qi < p.Nq ? qi : p.Nq - 1;
+        const uint8_t* mrow = p.mask + (int64_t)qm * p.Nkv;
+        if (p.mask_vec && key0 + 8 <= p.Nkv) {
+          u32x2 w = *reinterpret_cast<const u32x2*>(mrow + key0);
+          lo = w[0]; hi = w[1];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int key = key0 + j;
+            uint32_t byte = key < p.Nkv ? mrow[key] : 0u;
+            if (j < 4) lo |= byte << (8 * j); else hi |= byte << (8 * (j - 4));
+          }
+        }
+      }
+    };
     auto mask_block = [&](int mt, f32x16& sa, auto masked_c) {
       constexpr bool IDX = decltype(masked_c)::value;
       if constexpr (!IDX && MASK == kMaskNone) {
         return true;
+      } else if constexpr (!IDX && MASK == kMaskBits) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sa[r] = keep_if_bit(mw, 16 * mt + r, sa[r]);
+        return ((mw >> (16 * mt)) & 0xffffu) != 0u;
+      } else if constexpr (!IDX) {
+        // byte mask only (no tail or causal test on this tile): two instructions per score
+        uint32_t w[4];
+        mask_words(mt, 0, w[0], w[1]);
+        mask_words(mt, 1, w[2], w[3]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          sa[4 * q + 0] = keep_if_byte<0>(w[q], sa[4 * q + 0]);
+          sa[4 * q + 1] = keep_if_byte<1>(w[q], sa[4 * q + 1]);
+          sa[4 * q + 2] = keep_if_byte<2>(w[q], sa[4 * q + 2]);
+          sa[4 * q + 3] = keep_if_byte<3>(w[q], sa[4 * q + 3]);
+        }
+        return (w[0] | w[1] | w[2] | w[3]) != 0u;
       } else {
         bool vis[16];
 #pragma unroll
@@ -447,29 +537,14 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
           const int key = k0 + 32 * mt + 16 * (r >> 3) + kl + (r & 7);
           vis[r] = IDX ? (key < kend) & (!p.causal | (key <= qi)) : true;
         }
-        if constexpr (MASK != kMaskNone) {
+        if constexpr (MASK == kMaskBits) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) vis[r] = vis[r] & (((mw >> (16 * mt + r)) & 1u) != 0u);
+        } else if constexpr (MASK != kMaskNone) {
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            const int key0 = k0 + 32 * mt + 16 * hf + kl;   // 8 consecutive keys
-            uint32_t lo = 0, hi = 0;
-            if constexpr (MASK == kMaskLds) {
-              const u32x2 w = *reinterpret_cast<const u32x2*>(maddr[2 * mt + hf] + S * MTILE);
-              lo = w[0]; hi = w[1];
-            } else {
-              const int qm = qi < p.Nq ? qi : p.Nq - 1;
-              const uint8_t* mrow = p.mask + (int64_t)qm * p.Nkv;
-              if (p.mask_vec && key0 + 8 <= p.Nkv) {
-                u32x2 w = *reinterpret_cast<const u32x2*>(mrow + key0);
-                lo = w[0]; hi = w[1];
-              } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                  const int key = key0 + j;
-                  uint32_t byte = key < p.Nkv ? mrow[key] : 0u;
-                  if (j < 4) lo |= byte << (8 * j); else hi |= byte << (8 * (j - 4));
-                }
-              }
-            }
+            uint32_t lo, hi;
+            mask_words(mt, hf, lo, hi);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
               const uint32_t byte = (j < 4 ? (lo >> (8 * j)) : (hi >> (8 * (j - 4)))) & 0xFFu;
@@ -778,12 +853,13 @@ inline hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t s) {
 template <typename T, int D, int BN>
 inline hipError_t launch_fwd_mask(const FwdParams& p, bool split, hipStream_t s) {
   constexpr int W = fwd_waves<D>();
-  const int mask = p.mask == nullptr ? kMaskNone : (p.mask_lds ? kMaskLds : kMaskGlobal);
-  if (split) {
+  const int mask = p.mask_bits ? kMaskBits : (p.mask == nullptr ? kMaskNone : (p.mask_lds ? kMaskLds : kMaskGlobal));
+  if (split) {   // packed masks are rejected before this point
     if (mask == kMaskLds) return launch_fwd_t<T, D, BN, kMaskLds, true, W>(p, s);
     if (mask == kMaskGlobal) return launch_fwd_t<T, D, BN, kMaskGlobal, true, W>(p, s);
     return launch_fwd_t<T, D, BN, kMaskNone, true, W>(p, s);
   }
+  if (mask == kMaskBits) return launch_fwd_t<T, D, BN, kMaskBits, false, W>(p, s);
   if (mask == kMaskLds) return launch_fwd_t<T, D, BN, kMaskLds, false, W>(p, s);
   if (mask == kMaskGlobal) return launch_fwd_t<T, D, BN, kMaskGlobal, false, W>(p, s);
   return launch_fwd_t<T, D, BN, kMaskNone, false, W>(p, s);

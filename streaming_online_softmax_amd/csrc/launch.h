@@ -28,6 +28,8 @@ struct FwdParams {
                         // 16-byte aligned, (Nq + 256) * Nkv < 2^32)
   float scale_log2;     // log2(e) / sqrt(D)
   float v_scale;        // 8-bit V (attn_fwd_fp8v): value = decoded code * v_scale
+  const uint32_t* mask_bits;   // packed mask (unsplit only; replaces mask): [ceil(Nq/32)][n_kgroups][64]
+  int n_kgroups;        // ceil(Nkv / 64)
 };
 
 // Bandwidth-bound split-K decode producer (one workgroup per row-head and partition).
@@ -84,5 +86,8 @@ hipError_t launch_round(const float* x, void* y, int64_t n, int dtype, hipStream
 hipError_t launch_decode(const DecodeParams& p, int dtype, int D, bool fused, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, int depth, int out_dtype, hipStream_t s);
 int fwd_block_m();
+// attn_mask_pack: byte mask [Nq, Nkv] -> lane-order bits (include/attn.h); causal skips the
+// groups above the diagonal.
+hipError_t launch_mask_pack(const uint8_t* mask, int Nq, int Nkv, int causal, uint32_t* bits, hipStream_t s);
 
 }  // namespace attn

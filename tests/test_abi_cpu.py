@@ -15,7 +15,7 @@ def test_library_exports_every_declared_symbol():
     names = sa.declared_symbols()
     assert {"attn_fwd", "attn_fwd_splitk", "attn_fwd_splitk_fused", "attn_combine", "attn_softmax_rows",
             "attn_round", "attn_fwd_fp8v", "attn_fwd_ex", "attn_last_error", "attn_abi_version",
-            "attn_fwd_splitk_noalloc"} <= set(names)
+            "attn_fwd_splitk_noalloc", "attn_mask_pack", "attn_fwd_packed"} <= set(names)
     for n in names:
         assert hasattr(sa.lib(), n), n
 
@@ -47,6 +47,9 @@ def test_header_is_plain_c_and_cpp(lang, std, tmp_path):
                        "         attn_softmax_rows(0, 0, 1, 1, ATTN_FP32, ATTN_SOFTMAX_STREAMING, 0) == ATTN_E_NULL &&\n"
                        "         attn_fwd_fp8v(0, 0, 0, ATTN_FP8_E4M3, 1.0f, 0, 0, 1, 1, 1, 128, 0, 0, ATTN_BF16, 0) == ATTN_E_NULL &&\n"
                        "         attn_round(0, 0, 4, ATTN_BF16, 0) == ATTN_E_NULL &&\n"
+                       "         attn_mask_pack(0, 1, 1, 0, 0, 0) == ATTN_E_NULL &&\n"
+                       "         attn_fwd_packed(0, 0, 0, 0, 0, 1, 1, 1, 64, 0, 0, ATTN_BF16, 0) == ATTN_E_NULL &&\n"
+                       "         ATTN_MASK_BITS_WORDS(33, 65) == 256 && ATTN_MASK_BITS_WORDS(32, 64) == 64 &&\n"
                        "         attn_fwd_ex(0, 0) == ATTN_E_NULL && attn_last_error()[0] != 0 ? 0 : 1;\n"
                        "}\n")
         exe = tmp_path / "use"
@@ -60,7 +63,14 @@ def test_header_is_plain_c_and_cpp(lang, std, tmp_path):
 
 
 def test_abi_version():
-    assert sa.attn_abi_version() == 1
+    assert sa.attn_abi_version() == 2
+
+
+@pytest.mark.parametrize("nq,nkv", [(1, 1), (32, 64), (33, 64), (32, 65), (400, 400), (16384, 16384)])
+def test_mask_bits_words(nq, nkv):
+    """The binding's word count of a packed mask is the header's: one word per lane (64) per
+    32-row group and 64-key group."""
+    assert sa.mask_bits_words(nq, nkv) == -(-nq // 32) * -(-nkv // 64) * 64
 
 
 def test_binding_constants_match_the_header():
@@ -122,6 +132,19 @@ def rnd(x=A, y=A, n=64, dtype=0):
 
 def combine(o_p=A, l_p=A, out=A, lse=None, P=4, rows=1, heads=1, depth=64, out_dtype=2):
     return sa.lib().attn_combine(o_p, l_p, out, lse, P, rows, heads, depth, out_dtype, None)
+
+
+def pack(mask=A, Nq=64, Nkv=64, causal=0, bits=A):
+    return sa.lib().attn_mask_pack(mask, Nq, Nkv, causal, bits, None)
+
+
+def packed(q=A, k=A, v=A, out=A, lse=None, B=1, H=1, N=64, D=64, causal=0, bits=A, dtype=0):
+    return sa.lib().attn_fwd_packed(q, k, v, out, lse, B, H, N, D, causal, bits, dtype, None)
+
+
+def fwd_ex(mask=None, bits=None, block_n=0, D=64):
+    a = sa.FwdArgs(A, A, A, A, None, mask, 1, 1, 64, D, 0, 0, block_n, bits)
+    return sa.lib().attn_fwd_ex(ctypes.byref(a), None)
 
 
 @needs_no_gpu
@@ -192,6 +215,21 @@ def combine(o_p=A, l_p=A, out=A, lse=None, P=4, rows=1, heads=1, depth=64, out_d
     (lambda: combine(out=None), E_NULL),
     (lambda: combine(o_p=BAD), E_ALIGN),
     (lambda: combine(rows=0), E_SHAPE),
+    (lambda: pack(mask=None), E_NULL),
+    (lambda: pack(bits=None), E_NULL),
+    (lambda: pack(Nq=0), E_SHAPE),
+    (lambda: pack(Nkv=-1), E_SHAPE),
+    (lambda: pack(causal=2), E_SHAPE),
+    (lambda: pack(causal=1, Nkv=65), E_SHAPE),     # causal packing is square only
+    (lambda: pack(bits=A + 2), E_ALIGN),
+    (lambda: packed(bits=None), E_NULL),
+    (lambda: packed(bits=A + 2), E_ALIGN),
+    (lambda: packed(q=None), E_NULL),
+    (lambda: packed(D=48), E_UNSUP),
+    (lambda: packed(causal=3), E_SHAPE),
+    (lambda: fwd_ex(mask=A, bits=A), E_SHAPE),      # one mask form at a time
+    (lambda: fwd_ex(bits=A + 1), E_ALIGN),
+    (lambda: fwd_ex(bits=A, block_n=48), E_UNSUP),
 ])
 def test_reject_paths(call, code):
     rc = call()
