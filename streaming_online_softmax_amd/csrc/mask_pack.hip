@@ -5,6 +5,7 @@
 // registers per lane: register r of lane l is row l % 32, key 16 (r / 8) + 8 (l / 32) + r % 8.
 // One 32-bit word per lane then covers the lane's scores of 64 keys (two such blocks), so a
 // kernel reads 256 contiguous bytes per wave and 64 keys instead of 2 KiB of mask rows.
+// Bit e (0..15) of a 16-byte chunk's code is byte e being nonzero.
 #include "device.h"
 #include "launch.h"
 
@@ -19,40 +20,49 @@ __device__ __forceinline__ uint32_t nonzero_bytes4(uint32_t x) {
   return ((t * 0x00204081u) >> 21) & 0xfu;
 }
 
-// One wave per (row group g, key group c), four key groups per workgroup; lane l assembles word
-// (g, c, l).  Its row's keys 64 c + 16 j + 8 (l / 32) .. +8 (j = 0..3) go to bits 8 j .. 8 j + 7.
+// One workgroup per 32-row group g and 4 key groups (256 keys): the rows' 256-byte spans are
+// read in 16-byte chunks, consecutive threads taking consecutive chunks of a row, and each
+// chunk's nonzero bytes become 16 bits in LDS.  Wave w then assembles the words of key group
+// 4 cb + w: lane l takes row l % 32 and, for j = 0..3, bits 8 (l / 32) .. +8 of chunk 4 w + j
+// (keys 64 c + 16 j + 8 (l / 32) .. +8) as its bits 8 j .. 8 j + 7.
 __global__ __launch_bounds__(256) void mask_pack_kernel(const uint8_t* __restrict__ mask, int Nq, int Nkv,
                                                         int causal, int vec, int n_kg, int n_cb,
                                                         uint32_t* __restrict__ bits) {
-  const int lane = threadIdx.x & 63;
-  const int g = blockIdx.x / n_cb;
-  const int c = (blockIdx.x % n_cb) * 4 + (threadIdx.x >> 6);
-  if (c >= n_kg) return;
-  if (causal && 64 * c > 32 * g + 31) return;   // no key of the group is visible to these rows
-  const int row = 32 * g + (lane & 31);
-  uint32_t word = 0;
-  if (row < Nq) {
-    const uint8_t* mrow = mask + (int64_t)row * Nkv;
+  __shared__ uint16_t nz[32][16];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int g = blockIdx.x / n_cb, cb = blockIdx.x % n_cb;
+  if (causal && 256 * cb > 32 * g + 31) return;   // every key group of the workgroup above the diagonal
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key0 = 64 * c + 16 * j + 8 * (lane >> 5);
-      uint32_t b8 = 0;
-      if (vec && key0 + 8 <= Nkv) {
-        const u32x2 x = *reinterpret_cast<const u32x2*>(mrow + key0);
-        b8 = nonzero_bytes4(x[0]) | (nonzero_bytes4(x[1]) << 4);
+  for (int s = 0; s < 2; ++s) {
+    const int i = t + 256 * s, r = i >> 4, ch = i & 15;
+    const int row = 32 * g + r, key0 = 256 * cb + 16 * ch;
+    uint32_t b16 = 0;
+    if (row < Nq && key0 < Nkv) {
+      const uint8_t* src = mask + (int64_t)row * Nkv + key0;
+      if (vec && key0 + 16 <= Nkv) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(src);
+        b16 = nonzero_bytes4(x[0]) | (nonzero_bytes4(x[1]) << 4) | (nonzero_bytes4(x[2]) << 8) |
+              (nonzero_bytes4(x[3]) << 12);
       } else {
-        for (int e = 0; e < 8; ++e)
-          if (key0 + e < Nkv && mrow[key0 + e] != 0) b8 |= 1u << e;
+        for (int e = 0; e < 16; ++e)
+          if (key0 + e < Nkv && src[e] != 0) b16 |= 1u << e;
       }
-      word |= b8 << (8 * j);
     }
+    nz[r][ch] = (uint16_t)b16;
   }
+  __syncthreads();
+  const int c = 4 * cb + wave;
+  if (c >= n_kg || (causal && 64 * c > 32 * g + 31)) return;   // no key of the group is visible to these rows
+  const int r = lane & 31, h = lane >> 5;
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) word |= ((uint32_t)(nz[r][4 * wave + j] >> (8 * h)) & 0xffu) << (8 * j);
   bits[((int64_t)g * n_kg + c) * 64 + lane] = word;
 }
 
 hipError_t launch_mask_pack(const uint8_t* mask, int Nq, int Nkv, int causal, uint32_t* bits, hipStream_t s) {
   const int n_g = (Nq + 31) / 32, n_kg = (Nkv + 63) / 64, n_cb = (n_kg + 3) / 4;
-  const int vec = ((uintptr_t)mask % 8 == 0) && (Nkv % 8 == 0);
+  const int vec = ((uintptr_t)mask % 16 == 0) && (Nkv % 16 == 0);   // every row start 16-byte aligned
   const int64_t blocks = (int64_t)n_g * n_cb;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   mask_pack_kernel<<<(unsigned)blocks, 256, 0, s>>>(mask, Nq, Nkv, causal, vec, n_kg, n_cb, bits);
