@@ -530,12 +530,24 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
           sa[4 * q + 3] = keep_if_byte<3>(w[q], sa[4 * q + 3]);
         }
         return (w[0] | w[1] | w[2] | w[3]) != 0u;
+      } else if constexpr (MASK == kMaskNone || MASK == kMaskBits) {
+        // tail or causal tile: the keys visible by index (key < kend, and key <= qi when causal)
+        // are a prefix of each run of 8 consecutive keys, so each run's visibility is the low
+        // min(max(lim - first key, 0), 8) bits; then the packed mask, then the bit select
+        const int lim = p.causal ? min(kend, qi + 1) : kend;
+        const int rel = lim - (k0 + 32 * mt + kl);
+        const int n0 = min(max(rel, 0), 8), n1 = min(max(rel - 16, 0), 8);
+        uint32_t vis = ((1u << n0) - 1u) | (((1u << n1) - 1u) << 8);
+        if constexpr (MASK == kMaskBits) vis &= mw >> (16 * mt);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sa[r] = keep_if_bit(vis, r, sa[r]);
+        return vis != 0u;
       } else {
         bool vis[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * mt + 16 * (r >> 3) + kl + (r & 7);
-          vis[r] = IDX ? (key < kend) & (!p.causal | (key <= qi)) : true;
+          vis[r] = (key < kend) & (!p.causal | (key <= qi));
         }
         if constexpr (MASK == kMaskBits) {
 #pragma unroll
