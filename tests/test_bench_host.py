@@ -49,6 +49,21 @@ def test_combine_bytes(bench):
     assert bench.combine_bytes(P, RH, D, out_elem=4) == read + np.zeros((RH, D), np.float32).nbytes + RH * 4
 
 
+def test_mask_pack_bytes(bench):
+    """A causal pack of an N x N mask moves, for every 32-row group g and 64-key group c it
+    writes (those holding a key at or below some row of the group: 64 c <= 32 g + 31), the 32 x 64
+    mask bytes read and the 64 words written; counted here pair by pair over the mask instead."""
+    for n in (1, 31, 32, 64, 65, 200, 1000):
+        ng, nkg = -(-n // 32), -(-n // 64)
+        groups = set()
+        for i in range(ng * 32):
+            for c in range(nkg):
+                if 64 * c <= i:                 # some key of group c is visible to row i
+                    groups.add((i // 32, c))
+        assert bench.mask_pack_bytes(n) == len(groups) * (32 * 64 + 64 * 4), n
+    assert bench.mask_pack_bytes(16384) == 151_584_768
+
+
 def test_published_peaks(bench):
     assert bench.PEAK_BF16_TFLOPS == 2500.0 and bench.PEAK_HBM_GBS == 8000.0 and bench.PEAK_FP8_TFLOPS == 5000.0
     # a FLOP of the bf16 / FP8 half-and-half mix at both peaks
