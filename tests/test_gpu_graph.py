@@ -63,3 +63,42 @@ def test_captured_forward_split_combine_fused_replays(sa):
         for i, (t, r) in enumerate(zip(outs, ref)):
             assert torch.equal(t, r), f"replay {replay}: output {i} differs from the eager result"
         assert int(tk.abs().sum()) == 0, "tickets not returned to zero"
+
+
+def test_captured_mask_pack_and_packed_forward_replays(sa):
+    """attn_mask_pack then attn_fwd on the bits, captured: every replay repacks the mask (its
+    words cleared in between, the groups above the diagonal included) and gives the eager outputs
+    bitwise."""
+    N, H, D = 700, 2, 128
+    rng = si.rng_for(98, 0)
+    q, k, v = (si.cast(x, "bf16").to(DEV) for x in si.draw_qkv(rng, (1, N, H, D), (1, N, H, D)))
+    mask, _ = si.bernoulli_mask(rng, N, N, 3)
+    md = torch.from_numpy(mask).to(DEV)
+    bits = torch.zeros(sa.mask_bits_words(N, N), dtype=torch.int32, device=DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+
+    def step():
+        sa.attn_mask_pack(md, bits, causal=True)
+        sa.attn_fwd_packed(q, k, v, out, lse, causal=True, mask_bits=bits)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [out.clone(), lse.clone()]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for replay in range(3):
+        out.fill_(0)
+        lse.fill_(0)
+        bits.fill_(-1)                               # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), f"replay {replay} differs"
