@@ -483,10 +483,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
         for (int dt = 0; dt < DT; ++dt) oacc[dt] = E::mfma32(va[k2][dt], pb[k2], oacc[dt]);
     };
     // Masks (select to -inf).  Register r of block mt holds key
-    // k0 + 32*mt + 16*(r/8) + 8*(lane/32) + r%8 for query qi.  Returns whether any of the lane's
-    // 16 keys stays visible: the OR of the select conditions, which stay lane masks in scalar
-    // registers, so it costs scalar instructions only.
-    // the byte-mask words of block mt, keys 16*hf .. +8 (lo: bytes 0-3, hi: 4-7)
+    // k0 + 32*mt + 16*(r/8) + 8*(lane/32) + r%8 for query qi.  mask_block returns whether any of
+    // the lane's 16 keys stays visible (for the rescale test's "no reference yet" clause).
+    // The byte-mask words of block mt, keys 16*hf .. +8 (lo: bytes 0-3, hi: 4-7):
     auto mask_words = [&](int mt, int hf, uint32_t& lo, uint32_t& hi) {
       const int key0 = k0 + 32 * mt + 16 * hf + kl;   // 8 consecutive keys
       lo = 0; hi = 0;
@@ -549,10 +548,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
           const int key = k0 + 32 * mt + 16 * (r >> 3) + kl + (r & 7);
           vis[r] = (key < kend) & (!p.causal | (key <= qi));
         }
-        if constexpr (MASK == kMaskBits) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) vis[r] = vis[r] & (((mw >> (16 * mt + r)) & 1u) != 0u);
-        } else if constexpr (MASK != kMaskNone) {
+        if constexpr (MASK != kMaskNone) {
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
             uint32_t lo, hi;
@@ -866,7 +862,7 @@ template <typename T, int D, int BN>
 inline hipError_t launch_fwd_mask(const FwdParams& p, bool split, hipStream_t s) {
   constexpr int W = fwd_waves<D>();
   const int mask = p.mask_bits ? kMaskBits : (p.mask == nullptr ? kMaskNone : (p.mask_lds ? kMaskLds : kMaskGlobal));
-  if (split) {   // packed masks are rejected before this point
+  if (split) {   // no split entry point takes a packed mask
     if (mask == kMaskLds) return launch_fwd_t<T, D, BN, kMaskLds, true, W>(p, s);
     if (mask == kMaskGlobal) return launch_fwd_t<T, D, BN, kMaskGlobal, true, W>(p, s);
     return launch_fwd_t<T, D, BN, kMaskNone, true, W>(p, s);
