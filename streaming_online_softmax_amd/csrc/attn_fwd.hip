@@ -22,7 +22,7 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int BN, bool split, 
 
 template <typename T, int MASK, int FMT>
 static hipError_t launch_fwd_v8_t(const FwdParams& p, hipStream_t s) {
-  return launch_fwd_t<T, 128, 64, MASK, false, 8, FMT>(p, s);
+  return launch_fwd_t<T, 128, 128, MASK, false, 8, FMT>(p, s);
 }
 
 template <typename T, int FMT>

@@ -129,7 +129,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
   // V tiles: 2 bytes per element, or 1 with V8.  V8 rows (D bytes, 8 chunks) are swizzled by
   // chunk ^ (2 * ((row / 2) % 4)): the 8 rows x 2 chunks that one half-wave of a byte-transposing
   // read touches then cover the 64 banks exactly once.
-  static_assert(!V8 || (D == 128 && BN == 64 && !SPLIT), "the FP8 second product is built for D = 128, 64-key tiles");
+  static_assert(!V8 || (D == 128 && (BN == 64 || BN == 128) && !SPLIT), "the FP8 second product is built for D = 128, 64- or 128-key tiles");
+  static_assert(MASK != kMaskBits || BN <= 64, "a packed-mask word covers 64 keys");
   static_assert(MASK != kMaskBits || !SPLIT, "packed masks assume key tiles aligned to 64 keys");
   constexpr int RBV = V8 ? D : RB;      // bytes per V row in LDS
   constexpr int TILEV = BN * RBV;
@@ -684,7 +685,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
     // consumes all 64 keys at once), so the lazy-rescale test is taken per tile, on the lane's
     // weight sum over the tile (and on no reference yet while a key is visible).  Weights <= 2^TAU = 256
     // lie inside E4M3's range (448), so the round-to-nearest-even conversion never saturates.
-    auto weights8 = [&](const f32x16& sa, float mu, i32x8& pb8, int mt) {
+    auto weights8 = [&](const f32x16& sa, float mu, i32x8& pb8, int slot) {
       float ps = 0.f;
       float pw[16];
 #pragma unroll
@@ -696,26 +697,53 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
       for (int i = 0; i < 4; ++i) {
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(pw[4 * i], pw[4 * i + 1], 0, false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(pw[4 * i + 2], pw[4 * i + 3], w, true);
-        pb8[4 * mt + i] = w;
+        pb8[4 * slot + i] = w;
       }
       return ps;
     };
+    // block mt of the tile into slot (mt % 2) of the 64-key operand pb8
     auto sm_start8 = [&](int mt, f32x16& sa, i32x8& pb8, auto masked_c) {
       BlockSm st;
       st.any = mask_block(mt, sa, masked_c);
-      st.ps = weights8(sa, (m_run == kNegInf) ? 0.f : m_run, pb8, mt);
+      st.ps = weights8(sa, (m_run == kNegInf) ? 0.f : m_run, pb8, mt & 1);
       return st;
     };
-    auto read_v8 = [&](int dt) {
+    auto read_v8 = [&](int dt, int half) {   // keys 64 half .. 64 half + 63 of the tile
       typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
       i32x8 va;
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vaddr8[dt] + S * TILEV + 16 * cc * D));
+        const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vaddr8[dt] + S * TILEV + 64 * D * half + 16 * cc * D));
         va[2 * cc] = w[0];
         va[2 * cc + 1] = w[1];
       }
       return va;
+    };
+    // the rescale test of one 64-key operand on both of its blocks' weight sums; a raise rescales
+    // the state and redoes both blocks' weights
+    auto vote8 = [&](BlockSm& a, BlockSm& b, const f32x16& sa, const f32x16& sb, i32x8& pb8) {
+      ATTN_PIN(a.ps);
+      ATTN_PIN(b.ps);
+      const bool raise =
+          __builtin_amdgcn_ballot_w64((a.ps + b.ps > kTauPow) | ((m_run == kNegInf) & (a.any | b.any))) != 0;
+      if (raise) {
+        const float m_new = fmaxf(m_run, fmaxf(block_max(sa), block_max(sb)));
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);   // 0 from empty
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
+        const float mu = (m_run == kNegInf) ? 0.f : m_run;
+        a.ps = weights8(sa, mu, pb8, 0);
+        b.ps = weights8(sb, mu, pb8, 1);
+      }
+      l_run += a.ps + b.ps;
+    };
+    auto pv8 = [&](const i32x8& pb8, int half) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        // operand formats: A (V^T) E4M3 (0) or E5M2 (1), B (P) E4M3 (0)
+        oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(read_v8(dt, half), pb8, oacc[dt], V8 == 2 ? 1 : 0, 0, 0, 0, 0, 0);
     };
     auto tile_body8 = [&](auto masked_c) {
       u32x4 kf[KSTEPS];
@@ -724,34 +752,46 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES >= 8 || D >= 256) ? 1 : 2) void 
       __builtin_amdgcn_sched_barrier(0);
       read_k(1, kf);
       f32x16 s1 = qk(kf);
-      i32x8 pb8;
-      BlockSm st0 = sm_start8(0, s0, pb8, masked_c);
+      i32x8 pbA;
+      BlockSm st0 = sm_start8(0, s0, pbA, masked_c);
 #pragma unroll
       for (int i = 0; i < KSTEPS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
       }
-      BlockSm st1 = sm_start8(1, s1, pb8, masked_c);
-      ATTN_PIN(st0.ps);
-      ATTN_PIN(st1.ps);
-      const bool raise =
-          __builtin_amdgcn_ballot_w64((st0.ps + st1.ps > kTauPow) | ((m_run == kNegInf) & (st0.any | st1.any))) != 0;
-      if (raise) {
-        const float m_new = fmaxf(m_run, fmaxf(block_max(s0), block_max(s1)));
-        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);   // 0 from empty
-        l_run *= alpha;
+      if constexpr (MT == 2) {
+        BlockSm st1 = sm_start8(1, s1, pbA, masked_c);
+        vote8(st0, st1, s0, s1, pbA);
+        pv8(pbA, 0);
+      } else {
+        // 128-key tiles: the product of keys 0..63 runs beside block 2's softmax, so only
+        // block 3's softmax has no matrix work of its own wave beside it:
+        //   S_0; [S_1 || sm(S_0)]; [S_2 || sm(S_1)]; test; [O += V P_01, S_3 || sm(S_2)];
+        //   sm(S_3); test; O += V P_23
+        static_assert(MT == 4, "64- or 128-key tiles");
+        read_k(2, kf);
+        f32x16 s2 = qk(kf);
+        BlockSm st1 = sm_start8(1, s1, pbA, masked_c);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-        m_run = m_new;
-        const float mu = (m_run == kNegInf) ? 0.f : m_run;
-        st0.ps = weights8(s0, mu, pb8, 0);
-        st1.ps = weights8(s1, mu, pb8, 1);
+        for (int i = 0; i < KSTEPS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+        }
+        vote8(st0, st1, s0, s1, pbA);
+        pv8(pbA, 0);
+        read_k(3, kf);
+        f32x16 s3 = qk(kf);
+        i32x8 pbB;
+        BlockSm st2 = sm_start8(2, s2, pbB, masked_c);
+#pragma unroll
+        for (int i = 0; i < KSTEPS + DT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+        BlockSm st3 = sm_start8(3, s3, pbB, masked_c);
+        vote8(st2, st3, s2, s3, pbB);
+        pv8(pbB, 1);
       }
-      l_run += st0.ps + st1.ps;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        // operand formats: A (V^T) E4M3 (0) or E5M2 (1), B (P) E4M3 (0)
-        oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(read_v8(dt), pb8, oacc[dt], V8 == 2 ? 1 : 0, 0, 0, 0, 0, 0);
     };
     if constexpr (V8) {
       if (need_tail || need_causal) tile_body8(std::true_type{});
@@ -842,7 +882,7 @@ template <int D> constexpr int fwd_waves() { return D == 128 ? 8 : 4; }
 // is separate so that the others keep their single-block code.
 template <typename T, int D, int BN, int MASK, bool SPLIT, int WAVES, int V8 = 0>
 inline hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t s) {
-  constexpr int NSTAGES = WAVES == 8 ? 3 : 2;
+  constexpr int NSTAGES = WAVES == 8 && BN <= 64 ? 3 : 2;
   FwdParams p = p0;
   p.n_qblocks = (p.Nq + WAVES * kRowsPerWave - 1) / (WAVES * kRowsPerWave);
   const int64_t units = (int64_t)p.H * p.B * p.P;
