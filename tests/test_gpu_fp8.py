@@ -117,6 +117,30 @@ def test_fp8v_against_oracle(sa, N, causal, masked, dtype, scale):
     _check(sa, q, k, v, scale, causal, mask, dtype, what=f"N={N} causal={causal} mask={masked} {dtype}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_fp8v_staged_mask_full_tiles(sa, causal, dtype):
+    """N = 768: six full 128-key tiles, so the byte mask is staged through LDS (rows 16-byte
+    aligned) tile after tile, over several query blocks (paired when causal); every row against
+    O1, and bitwise equal to the same mask read from global memory (a copy 8 bytes off 16-byte
+    alignment)."""
+    N = 768
+    case = 300 + 2 * int(causal) + (dtype == "f16")
+    q, k, v = si.fp8v_inputs(B=2, H=2, N=N, case=case, dtype=dtype)
+    mask, _ = si.bernoulli_mask(si.rng_for(si.CFG_FP8V, 100 + case), N, N, N // 64)
+    _check(sa, q, k, v, 1.0, causal, mask, dtype, what=f"staged mask N={N} causal={causal} {dtype}")
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    m16 = torch.from_numpy(mask).to(DEV)
+    buf = torch.zeros(N * N + 8, dtype=torch.uint8, device=DEV)
+    m8 = buf[8:].view(N, N)
+    m8.copy_(m16)
+    assert m16.data_ptr() % 16 == 0 and m8.data_ptr() % 16 == 8
+    o1, l1 = sa.fwd_fp8v(qd, kd, vd, 1.0, causal=causal, mask=m16)
+    o2, l2 = sa.fwd_fp8v(qd, kd, vd, 1.0, causal=causal, mask=m8)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "staged != direct"
+
+
 E5M2_CASES = [(N, causal, masked, dtype) for N in (17, 200, 1000) for causal in (False, True)
               for masked in (False, True) for dtype in ("bf16", "f16")]
 
