@@ -178,3 +178,35 @@ def test_masked_long_context_packed_matches_bytes(sa):
     o2, l2 = sa.fwd(qd, kd, vd, causal=True, mask_bits=bits)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def _random_cases(n):
+    rng = si.rng_for(99, 0)
+    cases = []
+    for _ in range(n):
+        D = int(rng.choice([16, 32, 64, 128, 256]))
+        BN = int(rng.choice([32, 64])) if D <= 64 else 64
+        cases.append((int(rng.integers(1, 1500)), D, BN, bool(rng.integers(0, 2)), int(rng.integers(1, 3)),
+                      int(rng.integers(1, 4)), float(rng.choice([0.1, 0.5, 0.9]))))
+    return cases
+
+
+RANDOM_CASES = _random_cases(40)
+
+
+@pytest.mark.parametrize("N,D,BN,causal,B,H,density", RANDOM_CASES,
+                         ids=[f"N{c[0]}-D{c[1]}-BN{c[2]}-{'c' if c[3] else 'nc'}-B{c[4]}H{c[5]}-p{c[6]}"
+                              for c in RANDOM_CASES])
+def test_packed_matches_bytes_random_shapes(sa, N, D, BN, causal, B, H, density):
+    """Seeded random sizes (tile tails, partial query blocks and 32-row groups, paired causal
+    blocks at D = 128, both tile widths) and mask densities: the packed forward equals the
+    byte-mask forward bit for bit; the byte path is the one compared with the oracle elsewhere."""
+    rng = si.rng_for(99, N * 7 + D + BN + int(causal))
+    q, k, v = (si.cast(x, "bf16").to(DEV) for x in si.draw_qkv(rng, (B, N, H, D), (B, N, H, D)))
+    mask = (rng.random((N, N)) < density).astype(np.uint8)
+    md = torch.from_numpy(mask).to(DEV)
+    bits = sa.pack_mask(md, causal=causal)
+    o1, l1 = sa.fwd(q, k, v, causal=causal, mask=md, block_n=BN)
+    o2, l2 = sa.fwd(q, k, v, causal=causal, mask_bits=bits, block_n=BN)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
